@@ -1,0 +1,30 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    import oracle
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    return oracle
+
+
+@pytest.fixture(scope="session")
+def synth():
+    import dsa_synth
+
+    if not os.path.exists(dsa_synth.LIB_PATH):
+        dsa_synth.build()
+    return dsa_synth
