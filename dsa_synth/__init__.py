@@ -120,6 +120,7 @@ class Workload:
     topk: int
     sm_scale: float
     seed: int
+    table_seed: int = -1   # seed of the block-table shuffle; -1: use `seed`
 
     @property
     def n_seq(self) -> int:
@@ -167,18 +168,19 @@ def ragged_lengths(n: int, lo: int, hi: int, seed: int) -> tuple:
     return tuple(int(x) for x in out)
 
 
-def latent(name, phase, seq_lens, seed, topk=2048, block_size=64, H=128, H_idx=64) -> Workload:
+def latent(name, phase, seq_lens, seed, topk=2048, block_size=64, H=128, H_idx=64,
+           table_seed=-1) -> Workload:
     """The 576-wide shared-latent shape: V is the first 512 columns of each K row."""
     return Workload(name=name, phase=phase, seq_lens=tuple(seq_lens), block_size=block_size,
                     H=H, d_qk=576, d_v=512, separate_v=False, H_idx=H_idx, d_idx=128,
-                    topk=topk, sm_scale=1.0 / math.sqrt(576.0), seed=seed)
+                    topk=topk, sm_scale=1.0 / math.sqrt(576.0), seed=seed, table_seed=table_seed)
 
 
-def small_mqa(name, phase, seq_lens, seed, topk=64, block_size=16) -> Workload:
+def small_mqa(name, phase, seq_lens, seed, topk=64, block_size=16, table_seed=-1) -> Workload:
     """The small shape: 8 query heads on one K and one V head of width 64."""
     return Workload(name=name, phase=phase, seq_lens=tuple(seq_lens), block_size=block_size,
                     H=8, d_qk=64, d_v=64, separate_v=True, H_idx=4, d_idx=32, topk=topk,
-                    sm_scale=1.0 / 8.0, seed=seed)
+                    sm_scale=1.0 / 8.0, seed=seed, table_seed=table_seed)
 
 
 def workload(n: int) -> Workload:
@@ -200,7 +202,8 @@ def workload(n: int) -> Workload:
 def block_table(wl: Workload) -> np.ndarray:
     """[n_seq, max_blocks] int32; entries past a sequence's last block are 0."""
     perm = np.zeros(wl.pool_blocks, dtype=np.int32)
-    _check(lib().synth_permutation(perm.ctypes.data, wl.pool_blocks, wl.seed, TID_BT), "perm")
+    tseed = wl.seed if wl.table_seed < 0 else wl.table_seed
+    _check(lib().synth_permutation(perm.ctypes.data, wl.pool_blocks, tseed, TID_BT), "perm")
     bt = np.zeros((wl.n_seq, wl.max_blocks), dtype=np.int32)
     off = 0
     for b, nb in enumerate(wl.blocks_per_seq):

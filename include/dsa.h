@@ -1,0 +1,153 @@
+/*
+ * dsa.h — C ABI of libdsa.so: DSA sparse attention over a block-paged KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * The hot path has three stages (web page "Day-0 Adaptation of
+ * Trillion-Parameter MoE Models on Domestic GPUs", section 3 "Adapting
+ * Sparse Attention (DSA)"):
+ *   1. index selection: a low-dimensional indexer scores every past position
+ *      (dsa_index_score) and a block-wise Top-K keeps the K best positions
+ *      (dsa_topk), item (1);
+ *   2. the kept K/V rows are gathered from a paged cache through a block
+ *      table, item (2);
+ *   3. exact softmax attention runs over the kept rows only, with separate
+ *      prefill and decode kernels (dsa_sparse_attn_prefill,
+ *      dsa_sparse_attn_decode), item (3).
+ * The Top-K output layout is exactly what the attention calls read (page
+ * "Technical Path for Day-0 Adaptation of Trillion-Parameter Models on
+ * Domestic GPUs", section 3.1, requirement 1), and one block table maps the
+ * cache for every call (page "Day-0 Adaptation of Ultra-Large-Scale MoE
+ * Models on Heterogeneous AI Accelerators", section 4, cache layout
+ * alignment).
+ *
+ * Conventions for every call
+ *   - Memory: every pointer argument is DEVICE memory owned by the caller,
+ *     except `cache` (a host struct holding device pointers).  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Streams: work is enqueued on `stream` and is asynchronous; results are
+ *     valid once the stream has been synchronised.
+ *   - Errors: arguments are checked on the host before anything is launched;
+ *     a failing check returns its status and launches nothing.  Device
+ *     contents (block table entries, lengths, indices) are trusted: they are
+ *     not read on the host.  A launch failure returns DSA_ERR_HIP.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Shapes supported by the kernels (others return DSA_ERR_UNSUPPORTED):
+ *       indexer   (H_idx, d_idx) = (64, 128) or (4, 32);
+ *       attention (H, d_qk, d_v) = (128, 576, 512) with V the first 512
+ *                 columns of each K row (cache->v == NULL), or (8, 64, 64)
+ *                 with a separate V pool;
+ *       1 <= K <= 2048; any block_size >= 1; any lengths.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+  DSA_ERR_SHAPE = 2,        /* a size or stride is out of range or inconsistent */
+  DSA_ERR_UNSUPPORTED = 3,  /* no kernel for this head count / width            */
+  DSA_ERR_WORKSPACE = 4,    /* workspace_bytes below the matching *_workspace_size */
+  DSA_ERR_DEVICE = 5,       /* current device is not gfx950 or not usable       */
+  DSA_ERR_HIP = 6           /* a HIP launch failed                              */
+} dsa_status_t;
+
+typedef enum { DSA_PREFILL = 0, DSA_DECODE = 1 } dsa_phase_t;
+
+/* Block-paged cache (page 1, section 3 item (2)): position p of sequence b
+ * lives in physical block block_table[b * max_blocks_per_seq + p / block_size],
+ * slot p % block_size.  A pool row of block blk, slot s starts at element
+ * (blk * block_size + s) * row_stride.  All pointers are device memory. */
+typedef struct {
+  const uint16_t *kv;         /* bf16 key rows, d_qk columns used (the latent row when v == NULL) */
+  int64_t kv_row_stride;      /* elements between consecutive slots, >= d_qk                    */
+  const uint16_t *v;          /* bf16 value rows (d_v columns), or NULL: V = first d_v columns of kv */
+  int64_t v_row_stride;       /* elements between slots of v (ignored when v == NULL)           */
+  const uint16_t *k_idx;      /* bf16 indexer keys, one row of d_idx per position               */
+  int64_t k_idx_row_stride;   /* elements between slots of k_idx, >= d_idx                      */
+  const int32_t *block_table; /* [n_seq, max_blocks_per_seq] physical block ids                  */
+  const int32_t *seq_lens;    /* [n_seq] cached positions per sequence (current token included) */
+  int32_t n_seq;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;         /* blocks in each pool                                            */
+  int32_t block_size;
+  int32_t d_qk, d_v, d_idx;
+} dsa_paged_cache_t;
+
+/* Index score (page 1, section 3 item (1): low-dimensional similarity
+ * scoring of every past position).
+ *   scores[i * ld + s] = sum_h w[i*H_idx + h] * max(0, q_idx[i,h,:] . k_idx(seq_i, s))
+ * for every candidate s = 0 .. pos_i of query i; other entries of the row are
+ * left unspecified.  Sums are exact for integer-valued inputs below 2^24.
+ *   DSA_DECODE:  n_q == cache->n_seq; query i is the last cached token of
+ *                sequence i (pos_i = seq_lens[i] - 1); prefill_seq and
+ *                prefill_pos0 are ignored.  ld >= max seq_lens.
+ *   DSA_PREFILL: query i is position prefill_pos0 + i of sequence
+ *                prefill_seq (chunked causal prefill); ld >= prefill_pos0 + n_q.
+ * q_idx: bf16 [n_q, H_idx, d_idx]; w: fp32 [n_q, H_idx]; scores: fp32 [n_q, ld]. */
+dsa_status_t dsa_index_score(const dsa_paged_cache_t *cache, dsa_phase_t phase,
+                             const uint16_t *q_idx, const float *w, int32_t n_q, int32_t H_idx,
+                             int32_t prefill_seq, int32_t prefill_pos0, float *scores, int64_t ld,
+                             hipStream_t stream);
+
+/* Workspace bytes dsa_topk needs for these sizes (0 is possible). */
+size_t dsa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t K);
+
+/* Top-K (page 1, section 3 item (1): block-wise scoring, intra-block
+ * reduction, cross-block merge; no global sort).  Row i has n_i candidates
+ * scores[i * ld + 0 .. n_i - 1], where n_i = n_valid[i] if n_valid != NULL,
+ * else causal_base + i + 1 (the rows of a causal prefill chunk).
+ * idx[i * K + r] receives the positions of the K largest scores, equal scores
+ * ordered by lower position first, listed in ascending position order;
+ * when n_i < K the row holds 0 .. n_i - 1 followed by -1.
+ * -0.0 and +0.0 compare equal; NaN scores are not allowed.
+ * n_i must satisfy 0 <= n_i <= ld (not checked: device data). */
+dsa_status_t dsa_topk(const float *scores, int64_t ld, int32_t n_q, int32_t K,
+                      const int32_t *n_valid, int32_t causal_base, int32_t *idx, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes dsa_sparse_attn_decode needs (split-K partial results). */
+size_t dsa_sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t K, int32_t d_v);
+
+/* Sparse attention, decode path (page 1, section 3 item (3): one token per
+ * step, bandwidth bound).  Query b is the last token of sequence b
+ * (B == cache->n_seq).  For every head h:
+ *   l_j = sm_scale * q[b,h,:] . K_j,  p = softmax(l) over the kept j,
+ *   out[b,h,:] = sum_j p_j V_j,       lse[b,h] = ln sum_j exp(l_j)
+ * where j runs over idx[b*K + r] for r < min(K, seq_lens[b]) with
+ * idx >= 0; entries < 0 are skipped.  K_j / V_j are rows of position j read
+ * through the block table.  q: bf16 [B, H, d_qk]; out: bf16 [B, H, d_v];
+ * lse: fp32 [B, H] or NULL.  A row with nothing kept gives out = 0,
+ * lse = -inf.  The work is split over the kept positions and merged by
+ * log-sum-exp; `workspace` holds the partial results. */
+dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t *cache, const uint16_t *q,
+                                    const int32_t *idx, int32_t B, int32_t H, int32_t K,
+                                    float sm_scale, uint16_t *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse attention, prefill path (page 1, section 3 item (3): many queries,
+ * compute bound).  Query t is position pos0 + t of sequence `seq`; same
+ * formula as decode, with j over idx[t*K + r] for r < min(K, pos0 + t + 1)
+ * and idx >= 0.  q: bf16 [T, H, d_qk]; out: bf16 [T, H, d_v]; lse: fp32
+ * [T, H] or NULL.  No workspace. */
+dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t *cache, const uint16_t *q,
+                                     const int32_t *idx, int32_t T, int32_t H, int32_t K,
+                                     int32_t seq, int32_t pos0, float sm_scale, uint16_t *out,
+                                     float *lse, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *dsa_status_string(dsa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

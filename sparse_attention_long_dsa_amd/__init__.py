@@ -1,0 +1,299 @@
+"""DSA sparse attention on MI355X (gfx950): Python binding of libdsa.so.
+
+Argument marshalling only.  Every step of the hot path (index score, Top-K,
+paged gather, sparse attention) runs in the library's HIP kernels; torch
+provides device memory and the current stream.  There is no fallback: if
+libdsa.so is missing or cannot load, importing the functions below raises.
+
+The C ABI is declared in include/dsa.h; the names here match it:
+  index_score        -> dsa_index_score
+  topk               -> dsa_topk
+  sparse_attn_decode -> dsa_sparse_attn_decode
+  sparse_attn_prefill-> dsa_sparse_attn_prefill
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip"]
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+               # keep packed-fp32 instructions out of the generated code
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+DSA_PREFILL, DSA_DECODE = 0, 1
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
+          4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP"}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libdsa.so in-tree with hipcc for gfx950."""
+    srcs = [os.path.join(_HERE, "csrc", s) for s in SOURCES]
+    cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, *srcs, "-o", LIB_PATH + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building libdsa.so failed:\n" + r.stderr)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    if verbose:
+        print("built", LIB_PATH)
+    return LIB_PATH
+
+
+class PagedCache(ctypes.Structure):
+    """Mirror of dsa_paged_cache_t."""
+    _fields_ = [("kv", ctypes.c_void_p), ("kv_row_stride", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_row_stride", ctypes.c_int64),
+                ("k_idx", ctypes.c_void_p), ("k_idx_row_stride", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("n_seq", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_idx", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdsa.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_size_t)
+        pc = ctypes.POINTER(PagedCache)
+        L.dsa_index_score.argtypes = [pc, i32, vp, vp, i32, i32, i32, i32, vp, i64, vp]
+        L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
+        L.dsa_topk_workspace_size.restype = sz
+        L.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, sz, vp]
+        L.dsa_sparse_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.dsa_sparse_attn_decode_workspace_size.restype = sz
+        L.dsa_sparse_attn_decode.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+        L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode,
+                  L.dsa_sparse_attn_prefill):
+            f.restype = i32
+        _lib = L
+    return _lib
+
+
+class DsaError(RuntimeError):
+    def __init__(self, code: int, call: str):
+        msg = lib().dsa_status_string(code).decode()
+        super().__init__(f"{call}: {STATUS.get(code, code)} ({msg})")
+        self.code = code
+
+
+def _check(code: int, call: str):
+    if code != 0:
+        raise DsaError(code, call)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    import torch
+
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Cache:
+    """A block-paged cache in device memory (tensors are referenced, not copied).
+
+    kv:          bf16 [num_blocks, block_size, d_qk] key rows (latent rows when v is None)
+    k_idx:       bf16 [num_blocks, block_size, d_idx] indexer keys
+    block_table: int32 [n_seq, max_blocks_per_seq]
+    seq_lens:    int32 [n_seq]
+    v:           bf16 [num_blocks, block_size, d_v] or None (V = kv[..., :d_v])
+    """
+
+    def __init__(self, kv, k_idx, block_table, seq_lens, v=None, d_v=None):
+        import torch
+
+        _need(kv, torch.bfloat16, "kv")
+        _need(k_idx, torch.bfloat16, "k_idx")
+        _need(block_table, torch.int32, "block_table")
+        _need(seq_lens, torch.int32, "seq_lens")
+        if v is not None:
+            _need(v, torch.bfloat16, "v")
+        nb, bs, d_qk = kv.shape
+        if d_v is None:
+            d_v = v.shape[-1] if v is not None else 512
+        self.tensors = (kv, k_idx, block_table, seq_lens, v)
+        self.c = PagedCache(kv.data_ptr(), d_qk, _ptr(v), v.shape[-1] if v is not None else 0,
+                            k_idx.data_ptr(), k_idx.shape[-1], block_table.data_ptr(),
+                            seq_lens.data_ptr(), block_table.shape[0], block_table.shape[1], nb,
+                            bs, d_qk, d_v, k_idx.shape[-1])
+
+    @property
+    def n_seq(self):
+        return self.c.n_seq
+
+
+def index_score(cache: Cache, q_idx, w, phase: int, prefill_seq: int = 0, prefill_pos0: int = 0,
+                ld: Optional[int] = None, out=None, stream=None):
+    """dsa_index_score: fp32 scores [n_q, ld]."""
+    import torch
+
+    _need(q_idx, torch.bfloat16, "q_idx")
+    _need(w, torch.float32, "w")
+    n_q, H_idx, _ = q_idx.shape
+    if ld is None:
+        ld = out.shape[1] if out is not None else None
+    if out is None:
+        out = torch.empty((n_q, ld), dtype=torch.float32, device=q_idx.device)
+    _need(out, torch.float32, "scores")
+    _check(lib().dsa_index_score(ctypes.byref(cache.c), phase, q_idx.data_ptr(), w.data_ptr(), n_q,
+                                 H_idx, prefill_seq, prefill_pos0, out.data_ptr(), out.shape[1],
+                                 _stream(stream)), "dsa_index_score")
+    return out
+
+
+def topk_workspace(n_q: int, ld: int, K: int, device="cuda"):
+    import torch
+
+    n = lib().dsa_topk_workspace_size(n_q, ld, K)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def topk(scores, K: int, n_valid=None, causal_base: int = 0, out=None, workspace=None,
+         stream=None):
+    """dsa_topk: int32 [n_q, K] ascending kept positions, -1 padded."""
+    import torch
+
+    _need(scores, torch.float32, "scores")
+    n_q, ld = scores.shape
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid")
+    if out is None:
+        out = torch.empty((n_q, K), dtype=torch.int32, device=scores.device)
+    _need(out, torch.int32, "idx")
+    if workspace is None:
+        workspace = topk_workspace(n_q, ld, K, scores.device)
+    _check(lib().dsa_topk(scores.data_ptr(), ld, n_q, K, _ptr(n_valid), causal_base,
+                          out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                          _stream(stream)), "dsa_topk")
+    return out
+
+
+def decode_workspace(B: int, H: int, K: int, d_v: int, device="cuda"):
+    import torch
+
+    n = lib().dsa_sparse_attn_decode_workspace_size(B, H, K, d_v)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def sparse_attn_decode(cache: Cache, q, idx, sm_scale: float, out=None, lse=None,
+                       workspace=None, want_lse: bool = True, stream=None):
+    """dsa_sparse_attn_decode: (bf16 out [B, H, d_v], fp32 lse [B, H])."""
+    import torch
+
+    _need(q, torch.bfloat16, "q")
+    _need(idx, torch.int32, "idx")
+    B, H, _ = q.shape
+    K = idx.shape[1]
+    d_v = cache.c.d_v
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, H, K, d_v, q.device)
+    _check(lib().dsa_sparse_attn_decode(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), B, H,
+                                        K, float(sm_scale), out.data_ptr(), _ptr(lse),
+                                        workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "dsa_sparse_attn_decode")
+    return out, lse
+
+
+def sparse_attn_prefill(cache: Cache, q, idx, seq: int, pos0: int, sm_scale: float, out=None,
+                        lse=None, want_lse: bool = True, stream=None):
+    """dsa_sparse_attn_prefill: (bf16 out [T, H, d_v], fp32 lse [T, H])."""
+    import torch
+
+    _need(q, torch.bfloat16, "q")
+    _need(idx, torch.int32, "idx")
+    T, H, _ = q.shape
+    K = idx.shape[1]
+    d_v = cache.c.d_v
+    if out is None:
+        out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check(lib().dsa_sparse_attn_prefill(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), T, H,
+                                         K, seq, pos0, float(sm_scale), out.data_ptr(), _ptr(lse),
+                                         _stream(stream)), "dsa_sparse_attn_prefill")
+    return out, lse
+
+
+class DecodeStep:
+    """One decode step over a batch (index score -> Top-K -> sparse attention)
+    with every buffer allocated once up front."""
+
+    def __init__(self, cache: Cache, B: int, H: int, H_idx: int, K: int, ld: int, d_v: int,
+                 device="cuda"):
+        import torch
+
+        self.cache, self.K = cache, K
+        self.scores = torch.empty((B, ld), dtype=torch.float32, device=device)
+        self.idx = torch.empty((B, K), dtype=torch.int32, device=device)
+        self.out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.ws_topk = topk_workspace(B, ld, K, device)
+        self.ws_attn = decode_workspace(B, H, K, d_v, device)
+
+    def __call__(self, q, q_idx, w, sm_scale: float, stream=None):
+        c = self.cache
+        index_score(c, q_idx, w, DSA_DECODE, out=self.scores, stream=stream)
+        topk(self.scores, self.K, n_valid=c.tensors[3], out=self.idx, workspace=self.ws_topk,
+             stream=stream)
+        sparse_attn_decode(c, q, self.idx, sm_scale, out=self.out, lse=self.lse,
+                           workspace=self.ws_attn, stream=stream)
+        return self.out, self.lse
+
+
+class PrefillStep:
+    """Causal prefill of positions pos0 .. pos0+T-1 of one sequence."""
+
+    def __init__(self, cache: Cache, T: int, H: int, K: int, d_v: int, pos0: int = 0,
+                 device="cuda"):
+        import torch
+
+        self.cache, self.K, self.T, self.pos0 = cache, K, T, pos0
+        ld = pos0 + T
+        self.scores = torch.empty((T, ld), dtype=torch.float32, device=device)
+        self.idx = torch.empty((T, K), dtype=torch.int32, device=device)
+        self.out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.ws_topk = topk_workspace(T, ld, K, device)
+
+    def __call__(self, q, q_idx, w, sm_scale: float, seq: int = 0, stream=None):
+        c = self.cache
+        index_score(c, q_idx, w, DSA_PREFILL, prefill_seq=seq, prefill_pos0=self.pos0,
+                    out=self.scores, stream=stream)
+        topk(self.scores, self.K, causal_base=self.pos0, out=self.idx, workspace=self.ws_topk,
+             stream=stream)
+        sparse_attn_prefill(c, q, self.idx, seq, self.pos0, sm_scale, out=self.out, lse=self.lse,
+                            stream=stream)
+        return self.out, self.lse

@@ -1,0 +1,83 @@
+// Shared device helpers for the gfx950 DSA kernels: bf16 <-> fp32, MFMA
+// operand types, wave64 reductions and the paged-cache row lookup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Two floats -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// D = A(16x32) * B(32x16) + C on the gfx950 matrix cores, bf16 in, fp32 out.
+// Operand layout (wave64): lane l holds row/column (l & 15) and the 8
+// consecutive k-slots 8*(l >> 4) .. +7; the result lane l holds column
+// (l & 15), rows 4*(l >> 4) .. +3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// The same shape with fp16 operands.
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Physical pool row of logical position `pos` of the sequence whose block
+// table row is `bt_row`.
+__device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt_row, int bs, int pos) {
+  return (int64_t)bt_row[pos / bs] * bs + pos % bs;
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Order-preserving map of fp32 onto uint32: larger float -> larger key.
+// -0.0 is folded onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

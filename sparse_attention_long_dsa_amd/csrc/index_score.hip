@@ -1,0 +1,250 @@
+// Indexer scoring for DSA (web page "Day-0 Adaptation of Trillion-Parameter
+// MoE Models on Domestic GPUs", section 3 item (1): a low-dimensional
+// similarity score for every past position, ahead of Top-K filtering).
+//
+//   score(i, s) = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx(s,:))
+//
+// The per-head dot products are a dense contraction and run on the gfx950
+// matrix cores: one MFMA 16x16x32 (bf16 in, fp32 accumulate) takes 16 heads
+// (rows, from the query) against 16 positions (columns, from the indexer-key
+// cache).  The ReLU, head weight and head sum are a VALU epilogue on the
+// accumulators followed by a two-step cross-lane sum.  With integer-valued
+// inputs every partial sum is an integer below 2^24, so fp32 gives the exact
+// score whatever the summation order.
+//
+// Decode (one query per sequence, item (3): bandwidth bound): each workgroup
+// streams one chunk of one sequence's indexer keys straight from HBM into
+// MFMA operand registers (a lane loads 16 contiguous bytes of one key row);
+// the query stays in registers.  Prefill (item (3): compute bound): each
+// workgroup stages a tile of keys in LDS once and reuses it for a block of
+// queries, so keys are read from HBM once per query block.
+#include "common.h"
+#include "host_util.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// ---------------------------------------------------------------- decode
+
+template <int H_IDX, int D_IDX, int UNROLL>
+__global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+  constexpr int HT = (H_IDX + 15) / 16;  // 16-head tiles
+  constexpr int KS = D_IDX / 32;         // 32-wide k-steps
+  const int b = blockIdx.y;
+  const int L = seq_lens[b];
+  const int t0 = blockIdx.x * chunk;
+  if (t0 >= L) return;
+  const int t1 = min(t0 + chunk, L);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // A operand: head row 16*ht + col, dims 32*ks + 8*grp .. +7.
+  bf16x8 qa[HT][KS];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = 16 * ht + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head < H_IDX)
+        v = *(const u32x4*)(q_idx + ((int64_t)b * H_IDX + head) * D_IDX + 32 * ks + 8 * grp);
+      qa[ht][ks] = as_bf16x8(v);
+    }
+  }
+  // Head weights of the accumulator rows this lane holds: 16*ht + 4*grp + i.
+  float wr[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = 16 * ht + 4 * grp + i;
+      wr[ht][i] = head < H_IDX ? w[(int64_t)b * H_IDX + head] : 0.f;
+    }
+
+  const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
+  float* out = scores + (int64_t)b * ld;
+  constexpr int kStep = kWaves * 16 * UNROLL;
+  for (int base = t0 + wave * 16 * UNROLL; base < t1; base += kStep) {
+    u32x4 kb[UNROLL][KS];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int tok = base + 16 * u + col;
+      if (tok < t1) {
+        const uint16_t* row = k_idx + paged_row(bt_row, bs, tok) * k_stride + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[u][ks] = *(const u32x4*)(row + 32 * ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[u][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht] = mfma16x16x32(qa[ht][ks], as_bf16x8(kb[u][ks]), acc[ht]);
+      float s = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += wr[ht][i] * fmaxf(acc[ht][i], 0.f);
+      s = wave_sum_xor_16_32(s);
+      const int tok = base + 16 * u + col;
+      if (grp == 0 && tok < t1) out[tok] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- prefill
+
+template <int H_IDX, int D_IDX, int QB, int KB>
+__global__ __launch_bounds__(kThreads) void index_score_prefill_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ bt_row,
+    int bs, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int n_q, int pos0,
+    float* __restrict__ scores, int64_t ld) {
+  constexpr int HT = (H_IDX + 15) / 16;
+  constexpr int KS = D_IDX / 32;
+  constexpr int ROW = D_IDX + 8;  // padded LDS row (elements)
+  constexpr int CH = D_IDX / 8;   // 16-byte chunks per key row
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[KB * ROW];
+
+  const int q0 = blockIdx.y * QB;
+  const int qend = min(q0 + QB, n_q);
+  const int k0 = blockIdx.x * KB;
+  const int last_pos = pos0 + qend - 1;  // largest query position of the block
+  if (k0 > last_pos) return;
+  const int kend = min(k0 + KB, last_pos + 1);
+
+  for (int c = threadIdx.x; c < KB * CH; c += kThreads) {
+    const int r = c / CH, ch = c % CH;
+    const int pos = k0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (pos < kend) v = *(const u32x4*)(k_idx + paged_row(bt_row, bs, pos) * k_stride + 8 * ch);
+    *(u32x4*)(ktile + r * ROW + 8 * ch) = v;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  for (int qi = q0 + wave; qi < qend; qi += kWaves) {
+    const int n = min(kend, pos0 + qi + 1) - k0;  // keys of this tile the query sees
+    if (n <= 0) continue;
+    bf16x8 qa[HT][KS];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int head = 16 * ht + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (head < H_IDX)
+          v = *(const u32x4*)(q_idx + ((int64_t)qi * H_IDX + head) * D_IDX + 32 * ks + 8 * grp);
+        qa[ht][ks] = as_bf16x8(v);
+      }
+    }
+    float wr[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = 16 * ht + 4 * grp + i;
+        wr[ht][i] = head < H_IDX ? w[(int64_t)qi * H_IDX + head] : 0.f;
+      }
+    float* out = scores + (int64_t)qi * ld + k0;
+    for (int g = 0; g * 16 < n; ++g) {
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kb =
+            as_bf16x8(*(const u32x4*)(ktile + (16 * g + col) * ROW + 32 * ks + 8 * grp));
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += wr[ht][i] * fmaxf(acc[ht][i], 0.f);
+      s = wave_sum_xor_16_32(s);
+      if (grp == 0 && 16 * g + col < n) out[16 * g + col] = s;
+    }
+  }
+}
+
+template <int H_IDX, int D_IDX>
+dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
+                                const uint16_t* q_idx, const float* w, int n_q, int seq, int pos0,
+                                float* scores, int64_t ld, hipStream_t stream) {
+  if (phase == DSA_DECODE) {
+    // Chunk so that about 2048 workgroups cover n_q * ld positions.
+    int64_t per = (int64_t)n_q * ld / 2048;
+    int chunk = 256;
+    while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
+    const int64_t nchunks = (ld + chunk - 1) / chunk;
+    if (nchunks > 0x7fffffff) return DSA_ERR_SHAPE;
+    hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX, 4>),
+                       dim3((unsigned)nchunks, (unsigned)n_q), dim3(kThreads), 0, stream,
+                       c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
+                       c->block_size, c->seq_lens, q_idx, w, scores, ld, chunk);
+  } else {
+    constexpr int QB = 64, KB = 128;
+    const int64_t nkt = ((int64_t)pos0 + n_q + KB - 1) / KB;
+    const int64_t nqb = ((int64_t)n_q + QB - 1) / QB;
+    hipLaunchKernelGGL((index_score_prefill_kernel<H_IDX, D_IDX, QB, KB>),
+                       dim3((unsigned)nkt, (unsigned)nqb), dim3(kThreads), 0, stream, c->k_idx,
+                       c->k_idx_row_stride,
+                       c->block_table + (int64_t)seq * c->max_blocks_per_seq, c->block_size,
+                       q_idx, w, n_q, pos0, scores, ld);
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phase_t phase,
+                                        const uint16_t* q_idx, const float* w, int32_t n_q,
+                                        int32_t H_idx, int32_t prefill_seq, int32_t prefill_pos0,
+                                        float* scores, int64_t ld, hipStream_t stream) {
+  using namespace dsa;
+  dsa_status_t st = check_cache_common(cache);
+  if (st != DSA_OK) return st;
+  if (!cache->k_idx || !q_idx || !w || !scores) return DSA_ERR_NULL;
+  if (phase != DSA_DECODE && phase != DSA_PREFILL) return DSA_ERR_SHAPE;
+  if (n_q < 1 || ld < 1 || cache->k_idx_row_stride < cache->d_idx) return DSA_ERR_SHAPE;
+  if (phase == DSA_DECODE) {
+    if (!cache->seq_lens) return DSA_ERR_NULL;
+    if (n_q != cache->n_seq) return DSA_ERR_SHAPE;
+  } else {
+    if (prefill_seq < 0 || prefill_seq >= cache->n_seq || prefill_pos0 < 0) return DSA_ERR_SHAPE;
+    if ((int64_t)prefill_pos0 + n_q > ld) return DSA_ERR_SHAPE;
+    if ((int64_t)prefill_pos0 + n_q > (int64_t)cache->max_blocks_per_seq * cache->block_size)
+      return DSA_ERR_SHAPE;
+  }
+  const bool big = H_idx == 64 && cache->d_idx == 128;
+  const bool small = H_idx == 4 && cache->d_idx == 32;
+  if (!big && !small) return DSA_ERR_UNSUPPORTED;
+  if (cache->k_idx_row_stride % 8 != 0) return DSA_ERR_UNSUPPORTED;  // 16-byte row alignment
+  st = check_device();
+  if (st != DSA_OK) return st;
+  if (big)
+    return launch_index_score<64, 128>(cache, phase, q_idx, w, n_q, prefill_seq, prefill_pos0,
+                                       scores, ld, stream);
+  return launch_index_score<4, 32>(cache, phase, q_idx, w, n_q, prefill_seq, prefill_pos0, scores,
+                                   ld, stream);
+}

@@ -1,0 +1,108 @@
+"""Shared pieces of the GPU parity tests: run the library on a device case,
+compute the oracle on a host case (or on sampled rows at full size), and
+compare to the stated bars.
+
+Bars: index scores and Top-K indices bit-exact (the integer-valued indexer
+inputs make every fp32 score exact); attention output (bf16) within max-abs
+1e-2 and mean-abs 1e-3 of the fp32 oracle; lse within 1e-2.
+"""
+import numpy as np
+import torch
+
+import dsa_synth
+import oracle
+import sparse_attention_long_dsa_amd as dsa
+
+ATOL_MAX, ATOL_MEAN, LSE_TOL = 1e-2, 1e-3, 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def cache_of(dc):
+    return dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=dc.wl.d_v)
+
+
+def gpu_decode(dc):
+    wl = dc.wl
+    step = dsa.DecodeStep(cache_of(dc), wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
+    out, lse = step(dc.q, dc.q_idx, dc.w, wl.sm_scale)
+    torch.cuda.synchronize()
+    return step
+
+
+def gpu_prefill(dc, pos0=0, T=None, seq=0):
+    """Causal prefill of positions pos0 .. pos0+T-1 (queries are those rows of dc.q)."""
+    wl = dc.wl
+    T = wl.seq_lens[0] - pos0 if T is None else T
+    step = dsa.PrefillStep(cache_of(dc), T, wl.H, wl.topk, wl.d_v, pos0=pos0)
+    step(dc.q[pos0:pos0 + T].contiguous(), dc.q_idx[pos0:pos0 + T].contiguous(),
+         dc.w[pos0:pos0 + T].contiguous(), wl.sm_scale, seq=seq)
+    torch.cuda.synchronize()
+    return step
+
+
+def assert_attention(got_out, got_lse, ref_out, ref_lse, what=""):
+    g = got_out.float().cpu().numpy() if torch.is_tensor(got_out) else got_out
+    err = np.abs(g - ref_out)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    assert err.max() <= ATOL_MAX, f"{what}: max|err| {err.max():.3e}"
+    assert err.mean() <= ATOL_MEAN, f"{what}: mean|err| {err.mean():.3e}"
+    if got_lse is not None:
+        gl = got_lse.cpu().numpy() if torch.is_tensor(got_lse) else got_lse
+        lerr = np.abs(gl - ref_lse)
+        assert lerr.max() <= LSE_TOL, f"{what}: lse err {lerr.max():.3e}"
+    return err.max(), err.mean()
+
+
+def assert_idx_rows_valid(idx, n_valid, K):
+    """Properties every Top-K row has at any size: ascending distinct positions
+    below n, exactly min(n, K) of them, then -1."""
+    idx = idx.cpu() if torch.is_tensor(idx) else torch.from_numpy(idx)
+    n_valid = torch.as_tensor(n_valid).cpu().long()
+    m = torch.clamp(n_valid, max=K)
+    ar = torch.arange(K)[None, :]
+    keep = ar < m[:, None]
+    assert (idx[~keep] == -1).all(), "padding must be -1"
+    v = torch.where(keep, idx.long(), torch.iinfo(torch.int64).max)
+    assert (idx[keep] >= 0).all()
+    assert (torch.where(keep, idx.long(), -1) < n_valid[:, None]).all()
+    d = v[:, 1:] - v[:, :-1]
+    k2 = keep[:, 1:]
+    assert (d[k2] > 0).all(), "positions must be strictly ascending"
+
+
+def assert_topk_consistent(scores, idx, n_valid, K):
+    """Every kept score >= every dropped score, and among scores equal to the
+    smallest kept one, the kept positions are the lowest (checked on device)."""
+    for i in range(idx.shape[0]):
+        n = int(n_valid[i])
+        if n <= K:
+            continue
+        row = scores[i, :n]
+        sel = idx[i].long()
+        mask = torch.zeros(n, dtype=torch.bool, device=row.device)
+        mask[sel] = True
+        tau = row[sel].min()
+        assert row[~mask].max() <= tau
+        ties = torch.nonzero(row == tau).flatten()
+        kept_ties = torch.nonzero(mask & (row == tau)).flatten()
+        assert torch.equal(kept_ties, ties[: kept_ties.numel()])
+
+
+def oracle_decode_sampled(wl, seqs):
+    """Oracle scores, Top-K, attention for decode queries of the listed
+    sequences, each computed from a private per-sequence pool."""
+    res = {}
+    for b in seqs:
+        L = wl.seq_lens[b]
+        lbt, k_idx, _, _ = dsa_synth.host_sequence_pools(wl, b)
+        q, q_idx, w = dsa_synth.host_query_rows(wl, b, 1)
+        sc = oracle.index_score(k_idx, lbt, wl.block_size, q_idx, w, [0], [L - 1], ld=L)
+        idx = oracle.topk(sc, [L], wl.topk)
+        _, _, kv, v = dsa_synth.host_sequence_pools(wl, b, kv_positions=idx[0])
+        out, lse = oracle.sparse_attn(kv, v, lbt, wl.block_size, q, [0], idx, wl.sm_scale,
+                                      d_v=wl.d_v)
+        res[b] = (sc[0], idx[0], out[0], lse[0])
+    return res

@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: libdsa.so loads, exports every function that
+include/dsa.h declares, and rejects bad arguments on the host before any
+launch (on a machine with no GPU, well-formed calls stop at the device check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_dsa_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.LIB_PATH):
+        dsa.build()
+    return dsa.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_attn_decode", "dsa_sparse_attn_prefill"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    cdll = ctypes.CDLL(dsa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(cdll, name), name
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert L.dsa_status_string(code)
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every call below returns before any device work
+
+
+def cache(**kw):
+    c = dict(kv=FAKE, kv_row_stride=576, v=None, v_row_stride=0, k_idx=FAKE, k_idx_row_stride=128,
+             block_table=FAKE, seq_lens=FAKE, n_seq=2, max_blocks_per_seq=4, num_blocks=8,
+             block_size=64, d_qk=576, d_v=512, d_idx=128)
+    c.update(kw)
+    return dsa.PagedCache(**c)
+
+
+def score(L, c, phase=dsa.DSA_DECODE, q=FAKE, w=FAKE, n_q=2, H=64, seq=0, pos0=0, out=FAKE, ld=256):
+    return L.dsa_index_score(ctypes.byref(c), phase, q, w, n_q, H, seq, pos0, out, ld, None)
+
+
+def test_index_score_validation(L):
+    assert score(L, cache(), q=None) == 1
+    assert score(L, cache(k_idx=None)) == 1
+    assert score(L, cache(block_table=None)) == 1
+    assert score(L, cache(seq_lens=None)) == 1
+    assert L.dsa_index_score(None, 1, FAKE, FAKE, 2, 64, 0, 0, FAKE, 256, None) == 1
+    assert score(L, cache(), n_q=3) == 2                    # decode: n_q must equal n_seq
+    assert score(L, cache(), ld=0) == 2
+    assert score(L, cache(), phase=7) == 2
+    assert score(L, cache(), phase=dsa.DSA_PREFILL, n_q=200, ld=256, pos0=100) == 2  # past ld
+    assert score(L, cache(), phase=dsa.DSA_PREFILL, seq=2) == 2
+    assert score(L, cache(), H=32) == 3
+    assert score(L, cache(d_idx=64, k_idx_row_stride=64)) == 3
+    assert score(L, cache(k_idx_row_stride=100)) == 2        # stride below width
+    assert score(L, cache()) == 5                            # well formed: no gfx950 here
+    assert score(L, cache(d_idx=32, k_idx_row_stride=32), H=4) == 5
+
+
+def test_topk_validation(L):
+    ws = L.dsa_topk_workspace_size(4, 1 << 20, 2048)
+    assert ws >= 4 * (1 << 20) * 8
+    assert L.dsa_topk_workspace_size(4, 8192, 2048) == 0     # short rows need no workspace
+    f = L.dsa_topk
+    assert f(None, 100, 4, 8, FAKE, 0, FAKE, None, 0, None) == 1
+    assert f(FAKE, 100, 4, 8, FAKE, 0, None, None, 0, None) == 1
+    assert f(FAKE, 100, 4, 0, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(FAKE, 100, 4, 2049, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(FAKE, 100, 0, 8, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(FAKE, 100, 4, 8, None, 97, FAKE, None, 0, None) == 2   # causal rows past ld
+    assert f(FAKE, 1 << 20, 4, 2048, FAKE, 0, FAKE, None, 0, None) == 4
+    assert f(FAKE, 1 << 20, 4, 2048, FAKE, 0, FAKE, FAKE, ws - 1, None) == 4
+    assert f(FAKE, 1 << 20, 4, 2048, FAKE, 0, FAKE, FAKE, ws, None) == 5
+    assert f(FAKE, 100, 4, 8, None, 96, FAKE, None, 0, None) == 5
+
+
+def test_attention_validation(L):
+    dec = L.dsa_sparse_attn_decode
+    pre = L.dsa_sparse_attn_prefill
+    ws = L.dsa_sparse_attn_decode_workspace_size(2, 128, 2048, 512)
+    assert ws > 0
+    c = cache()
+    assert dec(ctypes.byref(c), None, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 1
+    assert dec(ctypes.byref(c), FAKE, FAKE, 3, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 2
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 64, 2048, 0.1, FAKE, None, FAKE, ws, None) == 3
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 4096, 0.1, FAKE, None, FAKE, ws, None) == 2
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws - 1, None) == 4
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 5
+    sep = cache(v=FAKE, v_row_stride=64, d_qk=64, d_v=64, kv_row_stride=64)
+    assert dec(ctypes.byref(sep), FAKE, FAKE, 2, 8, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 5
+    assert dec(ctypes.byref(cache(v=FAKE, v_row_stride=512)), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE,
+               None, FAKE, ws, None) == 3                    # latent shape wants V inside K rows
+    assert pre(ctypes.byref(c), FAKE, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 5
+    assert pre(ctypes.byref(c), FAKE, FAKE, 300, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 2
+    assert pre(ctypes.byref(c), FAKE, FAKE, 100, 128, 2048, 5, 0, 0.1, FAKE, None, None) == 2
+    assert pre(ctypes.byref(c), None, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 1

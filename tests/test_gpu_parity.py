@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element on seeded inputs, at sizes the oracle finishes in seconds (several
+tiles, ragged tails, both Top-K paths, both shape families), plus edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsa_synth
+import oracle
+import sparse_attention_long_dsa_amd as dsa
+from tests.helpers import (assert_attention, assert_idx_rows_valid, assert_topk_consistent,
+                           gpu_decode, gpu_prefill, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    dsa.lib()
+
+
+def check_decode(wl, sample_rows=None):
+    say(f"[decode] {wl.name} lens={wl.seq_lens[:6]}... K={wl.topk} bs={wl.block_size}")
+    dc = dsa_synth.device_case(wl)
+    step = gpu_decode(dc)
+    hc = dsa_synth.host_case(wl)
+    sc, idx, out, lse = oracle.decode_step(hc)
+    g_sc = step.scores.cpu().numpy()
+    for b, L in enumerate(wl.seq_lens):
+        np.testing.assert_array_equal(g_sc[b, :L], sc[b, :L], err_msg=f"scores row {b}")
+    np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
+    mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name)
+    # attention alone, fed the oracle's indices
+    o2, l2 = dsa.sparse_attn_decode(step.cache, dc.q, torch.from_numpy(idx).cuda(), wl.sm_scale)
+    assert_attention(o2, l2, out, lse, wl.name + " (oracle idx)")
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+    return dc, step
+
+
+def test_tiny_decode_chain_and_determinism():
+    wl = dsa_synth.workload(1)
+    dc, step = check_decode(wl)
+    first = (step.idx.clone(), step.out.clone(), step.lse.clone())
+    step(dc.q, dc.q_idx, dc.w, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], step.idx)
+    assert torch.equal(first[1], step.out) and torch.equal(first[2], step.lse)
+
+
+def test_small_family_ragged_decode():
+    wl = dsa_synth.small_mqa("small_ragged", "decode", [1, 17, 64, 65, 1000, 2500], seed=21,
+                             topk=64, block_size=16)
+    check_decode(wl)
+
+
+def test_latent_decode_short_rows():
+    # rows <= 16384 take the one-workgroup-per-row Top-K path
+    wl = dsa_synth.latent("latent_short", "decode", [700, 2048, 2049, 5000, 9001], seed=22,
+                          topk=2048)
+    check_decode(wl)
+
+
+def test_latent_decode_long_rows():
+    # rows > 16384 take the multi-workgroup Top-K path
+    wl = dsa_synth.latent("latent_long", "decode", [1500, 17000, 40000], seed=23, topk=2048)
+    check_decode(wl)
+
+
+def test_latent_decode_odd_K_and_block():
+    wl = dsa_synth.latent("latent_oddK", "decode", [37, 300, 20001], seed=24, topk=37,
+                          block_size=16)
+    check_decode(wl)
+
+
+def test_block_table_invariance():
+    a = dsa_synth.latent("inv", "decode", [3000, 20000], seed=25, topk=512)
+    b = dsa_synth.latent("inv", "decode", [3000, 20000], seed=25, topk=512, table_seed=99)
+    assert not np.array_equal(dsa_synth.block_table(a), dsa_synth.block_table(b))
+    sa = gpu_decode(dsa_synth.device_case(a))
+    sb = gpu_decode(dsa_synth.device_case(b))
+    assert torch.equal(sa.idx, sb.idx)
+    assert torch.equal(sa.out, sb.out)
+
+
+def check_prefill(wl, pos0=0, T=None):
+    T = wl.seq_lens[0] - pos0 if T is None else T
+    say(f"[prefill] {wl.name} pos0={pos0} T={T} K={wl.topk}")
+    dc = dsa_synth.device_case(wl)
+    step = gpu_prefill(dc, pos0=pos0, T=T)
+    hc = dsa_synth.host_case(wl)
+    rows = np.arange(pos0, pos0 + T)
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, hc.q_idx[rows], hc.w[rows],
+                            np.zeros(T, np.int32), rows.astype(np.int32), ld=pos0 + T)
+    idx = oracle.topk(sc, rows + 1, wl.topk)
+    out, lse = oracle.sparse_attn(hc.kv, hc.v, hc.block_table, wl.block_size, hc.q[rows],
+                                  np.zeros(T, np.int32), idx, wl.sm_scale, d_v=wl.d_v)
+    g_sc = step.scores.cpu().numpy()
+    for t in range(T):
+        n = pos0 + t + 1
+        assert np.array_equal(g_sc[t, :n], sc[t, :n]), f"scores row {t}"
+    np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
+    mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name)
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+
+
+def test_latent_prefill():
+    check_prefill(dsa_synth.latent("prefill_latent", "prefill", [700], seed=31, topk=256))
+
+
+def test_latent_prefill_chunk():
+    check_prefill(dsa_synth.latent("prefill_chunk", "prefill", [700], seed=32, topk=200),
+                  pos0=300, T=400)
+
+
+def test_small_family_prefill():
+    check_prefill(dsa_synth.small_mqa("prefill_small", "prefill", [333], seed=33, topk=64,
+                                      block_size=16))
+
+
+# ----------------------------------------------------------------------------- Top-K alone
+
+def _topk_case(scores, n_valid, K):
+    d_sc = torch.from_numpy(scores).cuda()
+    d_nv = torch.from_numpy(np.asarray(n_valid, np.int32)).cuda()
+    got = dsa.topk(d_sc, K, n_valid=d_nv)
+    torch.cuda.synchronize()
+    want = oracle.topk(scores, np.asarray(n_valid, np.int32), K)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+    assert_idx_rows_valid(got, n_valid, K)
+
+
+@pytest.mark.parametrize("ld", [3000, 50000])
+def test_topk_ties_and_special_rows(ld):
+    rng = np.random.default_rng(ld)
+    rows = [
+        np.full(ld, 7.0),                                  # all equal
+        rng.integers(0, 2, ld).astype(np.float64),         # two values
+        np.arange(ld, dtype=np.float64),                   # increasing
+        np.arange(ld, dtype=np.float64)[::-1].copy(),      # decreasing
+        rng.integers(-50, 50, ld).astype(np.float64),      # negative and positive ties
+        np.where(rng.random(ld) < 0.5, 0.0, -0.0),         # signed zeros compare equal
+        rng.normal(size=ld) * 1e30,                        # wide exponents
+        rng.normal(size=ld).astype(np.float32).astype(np.float64) * 1e-30,
+    ]
+    scores = np.stack(rows).astype(np.float32)
+    n_valid = [ld, ld - 1, ld, 2100, ld // 2, ld, 2049, ld]
+    for K in (1, 2048, 777):
+        _topk_case(scores, n_valid, K)
+
+
+def test_topk_short_rows_with_fewer_candidates_than_K():
+    scores = np.random.default_rng(5).integers(0, 9, (6, 4096)).astype(np.float32)
+    _topk_case(scores, [0, 1, 63, 64, 65, 4096], 64)
+
+
+def test_topk_causal_rows():
+    T = 3000
+    scores = np.random.default_rng(6).integers(0, 30, (T, T)).astype(np.float32)
+    got = dsa.topk(torch.from_numpy(scores).cuda(), 128, causal_base=0)
+    want = oracle.topk(scores, np.arange(1, T + 1, dtype=np.int32), 128)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
