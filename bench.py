@@ -9,6 +9,13 @@ token causal prefill is measured too and reported in the "prefill" object.
 
 Inputs are seeded synthetic data generated directly in HBM before timing.
 Prints one JSON line (see --help for the options).
+
+Two helper modes feed the roofline's "traffic" figure:
+  bench.py --calibrate-copy     a plain 1 GiB device copy (counter calibration)
+  bench.py --write-traffic F W CF CW
+                                fold rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+                                CSVs of the step (F, W) and of the copy (CF, CW)
+                                into profiles/index_score_decode_traffic.json
 """
 import argparse
 import hashlib
@@ -165,7 +172,63 @@ def cpu_baseline(wl, budget_s, log):
                       f"not timed"}
 
 
+COPY_BYTES = 1 << 30  # plain-copy calibration size
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES, three times: the counter
+    reading of this kernel is the scale for FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    torch.cuda.set_device(0)
+    a = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}))
+
+
+def _pmc_per_dispatch(csv_path, counter, name_part):
+    """Mean per-dispatch value of `counter` for kernels whose name contains
+    name_part, from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals.setdefault(r["Dispatch_Id"], 0.0)
+            vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {name_part} in {csv_path}")
+    return sum(vals.values()) / len(vals)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cname="copyBuffer"):
+    """Fold two counter runs of the decode step and two of the plain copy into
+    profiles/index_score_decode_traffic.json (HBM bytes per launch).  `cname`
+    names the copy kernel (the runtime's device-to-device copy)."""
+    kname = "index_score_decode_kernel"
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kname)
+    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kname)
+    cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", cname)
+    cw = _pmc_per_dispatch(copy_write_csv, "WRITE_SIZE", cname)
+    f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
+    out = {"kernel": "index_score_decode", "workload": "ragged_decode_B64_L4K-128K",
+           "fetch_raw": f, "write_raw": w, "copy_fetch_raw": cf, "copy_write_raw": cw,
+           "fetch_bytes": f * f_scale, "write_bytes": w * w_scale,
+           "bytes_per_launch": f * f_scale + w * w_scale,
+           "source_sha256": sha(INDEX_SRC)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--calibrate-copy":
+        return calibrate_copy()
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
+        return write_traffic(*sys.argv[2:])
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)

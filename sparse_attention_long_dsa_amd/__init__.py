@@ -21,7 +21,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip"]
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # keep packed-fp32 instructions out of the generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -30,13 +30,30 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPP
           4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP"}
 
 
+# Per-source extra flags.  The attention kernel keeps its MFMA accumulators
+# in arch VGPRs: with accumulators in AGPRs the compiler copies all of O
+# between the two register files on every tile.
+EXTRA_FLAGS = {"sparse_attn.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libdsa.so in-tree with hipcc for gfx950."""
-    srcs = [os.path.join(_HERE, "csrc", s) for s in SOURCES]
-    cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, *srcs, "-o", LIB_PATH + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("building libdsa.so failed:\n" + r.stderr)
+    """Compile libdsa.so in-tree with hipcc for gfx950 (one object per source)."""
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c",
+                   os.path.join(_HERE, "csrc", src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compiling {src} failed:\n" + r.stderr)
+            objs.append(obj)
+        cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-shared", *objs, "-o", LIB_PATH + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("linking libdsa.so failed:\n" + r.stderr)
     os.replace(LIB_PATH + ".tmp", LIB_PATH)
     if verbose:
         print("built", LIB_PATH)

@@ -71,9 +71,11 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
 
   const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
   float* out = scores + (int64_t)b * ld;
-  constexpr int kStep = kWaves * 16 * UNROLL;
-  for (int base = t0 + wave * 16 * UNROLL; base < t1; base += kStep) {
-    u32x4 kb[UNROLL][KS];
+  constexpr int kStep = kWaves * 16 * UNROLL;  // tokens per workgroup per round
+
+  // Two register buffers: the loads of the next round fly while this round's
+  // MFMAs and epilogue run.
+  auto load = [&](u32x4 (&kb)[UNROLL][KS], int base) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int tok = base + 16 * u + col;
@@ -86,6 +88,8 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
         for (int ks = 0; ks < KS; ++ks) kb[u][ks] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto compute = [&](const u32x4 (&kb)[UNROLL][KS], int base) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       f32x4 acc[HT];
@@ -105,6 +109,16 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
       const int tok = base + 16 * u + col;
       if (grp == 0 && tok < t1) out[tok] = s;
     }
+  };
+
+  u32x4 ka[UNROLL][KS], kb[UNROLL][KS];
+  int base = t0 + wave * 16 * UNROLL;
+  if (base < t1) load(ka, base);
+  for (; base < t1; base += 2 * kStep) {
+    if (base + kStep < t1) load(kb, base + kStep);
+    compute(ka, base);
+    if (base + 2 * kStep < t1) load(ka, base + 2 * kStep);
+    if (base + kStep < t1) compute(kb, base + kStep);
   }
 }
 
@@ -191,9 +205,11 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
                                 const uint16_t* q_idx, const float* w, int n_q, int seq, int pos0,
                                 float* scores, int64_t ld, hipStream_t stream) {
   if (phase == DSA_DECODE) {
-    // Chunk so that about 2048 workgroups cover n_q * ld positions.
-    int64_t per = (int64_t)n_q * ld / 2048;
-    int chunk = 256;
+    // Chunk so that about 4096 workgroups cover n_q * ld positions: about
+    // eight rounds of resident workgroups, so ragged lengths leave a short
+    // tail (each workgroup re-reads its 16 KB query from L2, not HBM).
+    int64_t per = (int64_t)n_q * ld / 4096;
+    int chunk = 1024;  // below this the per-workgroup query load dominates
     while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
     const int64_t nchunks = (ld + chunk - 1) / chunk;
     if (nchunks > 0x7fffffff) return DSA_ERR_SHAPE;

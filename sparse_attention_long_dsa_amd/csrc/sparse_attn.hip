@@ -6,25 +6,24 @@
 //
 // One workgroup takes one query and a group of 16*NW heads; all heads share
 // one K/V head (MQA, or the shared latent row where V is the first d_v
-// columns of K), so each gathered K/V tile in LDS serves every head of the
+// columns of K), so each gathered tile in LDS serves every head of the
 // group.  Per tile of 32 kept positions:
-//   gather:  32 rows go from HBM into an LDS K tile [token][d_qk] and a
-//            transposed fp16 LDS V tile [d_v][token]; each lane moves
-//            16-byte pieces of 8 rows and transposes the value part in
-//            registers;
+//   gather:  32 rows go from HBM into an LDS K tile [token][d_qk] (bf16);
+//            the loads of tile t+1 are in flight in registers while tile t
+//            computes;
 //   S^T = K Q^T   on MFMA 16x16x32 (A = K rows from LDS, B = q in registers;
 //                 the result lane holds one head and 8 tokens, so softmax
 //                 statistics need only two cross-lane steps);
 //   online softmax in the log2 domain with fp32 statistics;
-//   O^T += V^T P^T on MFMA (A = V^T from LDS, B = P^T straight from the S^T
-//                 accumulators, so P never leaves registers; O^T's lane
-//                 layout matches the per-head statistics, so rescaling needs
-//                 no data movement).
-// The P.V product runs in fp16, not bf16: bf16 values convert to fp16
-// exactly (|v| < 65504; magnitudes below 2^-24 flush to zero), and the
-// softmax weights in [0, 1] keep 11 significant bits instead of 8.  The
-// normaliser is the sum of the rounded weights, so one kept position
-// returns its V row exactly.
+//   O^T += V^T P^T on MFMA (A = V^T read straight from the row-major tile
+//                 with the gfx950 LDS transpose load - for the latent row V
+//                 is the first d_v columns of the K tile - and B = P^T
+//                 straight from the S^T accumulators, so P never leaves
+//                 registers; O^T's lane layout matches the per-head
+//                 statistics, so rescaling needs no data movement).
+// P enters the product as two bf16 MFMAs, P = P_hi + P_lo, which carries
+// 16 significant bits of each weight: the remaining error is the rounding of
+// the output to bf16.
 // Decode splits the kept positions of a query over several workgroups
 // (split-K) and merges the partial results by log-sum-exp in a second
 // kernel; prefill has enough queries to fill the chip without splitting.
@@ -40,49 +39,92 @@ constexpr int kTile = 32;  // kept positions per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Transpose an 8x8 block of bf16 into fp16: in[r] holds 8 consecutive bf16
-// columns of row r; out[c] receives column c of rows 0..7 as fp16.
-__device__ __forceinline__ void transpose8x8_to_f16(const u32x4 in[8], u32x4 out[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1;
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = in[2 * p][w], b = in[2 * p + 1][w];
-      o[p] = (c & 1) ? pack_f16x2(bf16_hi(a), bf16_hi(b)) : pack_f16x2(bf16_lo(a), bf16_lo(b));
-    }
-    out[c] = u32x4{o[0], o[1], o[2], o[3]};
-  }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// A 16x32 bf16 operand of V^T (rows: 16 value columns from dv0, k: tokens
+// 8*grp .. 8*grp+7) read from a row-major [token][column] LDS tile with two
+// transpose loads.  Within each group of 16 lanes, lane i names the 4
+// values V[t0 + i/4][dv0 + 4*(i%4) .. +3]; the hardware hands lane j the
+// values V[t0 .. t0+3][dv0 + j], i.e. 4 consecutive tokens of one column.
+__device__ __forceinline__ bf16x8 load_vt_operand(const uint16_t* tile, int row_elems, int dv0,
+                                                  int col, int grp) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const uint16_t* p0 = tile + (8 * grp + (col >> 2)) * row_elems + dv0 + 4 * (col & 3);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * row_elems));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return as_bf16x8(u32x4{ua.x, ua.y, ub.x, ub.y});
 }
 
-template <int NW, int D_QK, int D_V, bool SEP_V>
+template <int HB, int D_QK, int D_V, bool SEP_V>
 struct AttnCfg {
-  static constexpr int kThreads = NW * kWave;
-  static constexpr int kRow = D_QK + 8;    // K tile row (elements)
-  static constexpr int kVtRow = kTile + 8;  // V^T tile row (elements)
+  // HB blocks of 16 heads; two waves (a pair) per head block.
+  static constexpr int kWaves = 2 * HB;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kRow = D_QK + 8;    // K tile row (elements): the 16-byte pad keeps
+                                           // row reads and transpose loads conflict-free
+  static constexpr int kVRow = D_V + 8;    // V tile row (separate V pool only)
   static constexpr int kKS = D_QK / 32;    // k-steps of S
-  static constexpr int kDT = D_V / 16;     // 16-wide output tiles
+  static constexpr int kDTH = D_V / 32;    // 16-wide output tiles per wave (half of d_v)
   static constexpr int kKch = D_QK / 8;    // 16-byte chunks per K row
   static constexpr int kVch = D_V / 8;     // 16-byte chunks per V row
+  // Loading plan of one tile: 16-byte chunks, consecutive threads on
+  // consecutive chunks of a row.
+  static constexpr int kKChunks = kTile * kKch;
+  static constexpr int kVChunks = SEP_V ? kTile * kVch : 0;
+  static constexpr int kKC = (kKChunks + kThreads - 1) / kThreads;
+  static constexpr int kVC = SEP_V ? (kVChunks + kThreads - 1) / kThreads : 1;
+  static constexpr int kMaxTiles = 2048 / kTile;  // K <= 2048
 };
 
-template <int NW, int D_QK, int D_V, bool SEP_V>
-__global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
+// Registers holding one tile's gathered chunks between the global loads and
+// the LDS stores, so the loads of tile t+1 fly while tile t computes.
+template <class C>
+struct Staged {
+  u32x4 k[C::kKC];
+  u32x4 v[C::kVC];
+};
+
+// Work item of a workgroup: which query, head group and split.  Blocks are
+// dealt to the 8 XCDs round-robin by block id; every block of one query
+// gets the same block id modulo 8, so the K/V rows one head group pulls in
+// are L2 hits for the other.
+struct AttnItem {
+  int qi, hg, split;
+};
+__device__ __forceinline__ AttnItem attn_item(int n_q, int head_groups, int n_splits) {
+  const int per_query = head_groups * n_splits;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, j = b >> 3;
+  const int sub = j % per_query;
+  return AttnItem{(j / per_query) * 8 + xcd, sub % head_groups, sub / head_groups};
+}
+
+// Work split inside a workgroup.  Wave w serves head block hb = w % HB and
+// tile half h = w / HB.  For S the pair (hb, 0), (hb, 1) splits the 32
+// tokens of a tile (16 each); the pair then swaps per-head maxima and its
+// halves of P through LDS, and for O each wave of the pair takes one half
+// of the d_v value columns with all 32 tokens.  Two waves per SIMD hide each
+// other's LDS and barrier latency, and each wave holds only half of O.
+template <int HB, int D_QK, int D_V, bool SEP_V>
+__global__ __launch_bounds__(2 * HB * kWave) void sparse_attn_kernel(
     const uint16_t* __restrict__ kv, int64_t kv_stride, const uint16_t* __restrict__ vpool,
     int64_t v_stride, const int32_t* __restrict__ block_table, int max_blocks, int bs,
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ idx, int K, int H,
-    const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0, int tiles_per_split,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ idx, int n_q, int K, int H,
+    int head_groups, const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0,
+    int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
-  using C = AttnCfg<NW, D_QK, D_V, SEP_V>;
+  using C = AttnCfg<HB, D_QK, D_V, SEP_V>;
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kTile * C::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D_V * C::kVtRow];
-  __shared__ int32_t trow[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[SEP_V ? kTile * C::kVRow : 8];
+  __shared__ int32_t trows[C::kMaxTiles * kTile];  // physical rows of this block's range
+  __shared__ float xmax[HB][2][16];                 // per-head maximum of each half tile
+  __shared__ u32x4 xp[HB][2][kWave];                // P of each half tile: bf16 hi, lo
 
-  const int split = blockIdx.x;
-  const int head0 = blockIdx.y * 16 * NW;
-  const int qi = blockIdx.z;
+  const AttnItem it = attn_item(n_q, head_groups, n_splits);
+  if (it.qi >= n_q) return;
+  const int qi = it.qi, split = it.split;
+  const int head0 = it.hg * 16 * HB;
   const bool decode = seq_lens != nullptr;
   const int seq = decode ? qi : prefill_seq;
   const int n_cand = decode ? seq_lens[qi] : pos0 + qi + 1;
@@ -92,8 +134,20 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  const int hb = wave % HB, half = wave / HB;
   const int col = lane & 15, grp = lane >> 4;
-  const int head = head0 + 16 * wave + col;  // the head this lane's statistics belong to
+  const int head = head0 + 16 * hb + col;  // the head this lane's statistics belong to
+
+  const int n_tiles = (count + kTile - 1) / kTile;
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(n_tiles, t_begin + tiles_per_split);
+
+  // physical pool rows of every kept position of this block (-1: none)
+  for (int r = threadIdx.x; r < (t_end - t_begin) * kTile; r += C::kThreads) {
+    const int g = t_begin * kTile + r;
+    const int pos = g < count ? sel[g] : -1;
+    trows[r] = pos >= 0 ? (int32_t)paged_row(bt_row, bs, pos) : -1;
+  }
 
   // q as the B operand of S^T: dims 32*ks + 8*grp .. +7 of this lane's head
   bf16x8 qf[C::kKS];
@@ -104,130 +158,174 @@ __global__ __launch_bounds__(NW * kWave) void sparse_attn_kernel(
     qf[ks] = as_bf16x8(v);
   }
 
-  f32x4 o[C::kDT];
+  // Per-thread chunk coordinates (the same for every tile).
+  int k_row[C::kKC], k_off[C::kKC], v_row[C::kVC], v_off[C::kVC];
 #pragma unroll
-  for (int dt = 0; dt < C::kDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int c = 0; c < C::kKC; ++c) {
+    const int i = threadIdx.x + c * C::kThreads;
+    k_row[c] = i < C::kKChunks ? i / C::kKch : -1;
+    k_off[c] = 8 * (i % C::kKch);
+  }
+#pragma unroll
+  for (int c = 0; c < C::kVC; ++c) {
+    const int i = threadIdx.x + c * C::kThreads;
+    v_row[c] = SEP_V && i < C::kVChunks ? i / C::kVch : -1;
+    v_off[c] = 8 * (i % C::kVch);
+  }
+  __syncthreads();
 
-  const int n_tiles = (count + kTile - 1) / kTile;
-  const int t_begin = split * tiles_per_split;
-  const int t_end = min(n_tiles, t_begin + tiles_per_split);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int base = t * kTile;
-    if (threadIdx.x < kTile) {
-      const int r = base + threadIdx.x;
-      const int pos = r < count ? sel[r] : -1;
-      trow[threadIdx.x] = pos >= 0 ? (int32_t)paged_row(bt_row, bs, pos) : -1;
-    }
-    __syncthreads();
-
-    // ---- gather the tile into LDS
-    for (int u = threadIdx.x; u < 4 * C::kKch; u += C::kThreads) {
-      const int oct = u / C::kKch, ch = u % C::kKch;
-      u32x4 r[8];
+  // Gather loads are branch-free: a padded slot reads pool row 0 (always
+  // present) and its data is replaced by zeros.
+  Staged<C> st;
+  auto load_tile = [&](int t) {
+    const int32_t* tr = trows + (t - t_begin) * kTile;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = trow[8 * oct + j];
-        r[j] = row >= 0 ? *(const u32x4*)(kv + (int64_t)row * kv_stride + 8 * ch)
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *(u32x4*)(ktile + (8 * oct + j) * C::kRow + 8 * ch) = r[j];
-      if (!SEP_V && ch < C::kVch) {
-        u32x4 c8[8];
-        transpose8x8_to_f16(r, c8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x4*)(vt + (8 * ch + e) * C::kVtRow + 8 * oct) = c8[e];
-      }
+    for (int c = 0; c < C::kKC; ++c) {
+      const int row = k_row[c] >= 0 ? tr[k_row[c]] : -1;
+      const u32x4 v = *(const u32x4*)(kv + (int64_t)max(row, 0) * kv_stride + k_off[c]);
+      st.k[c] = row >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
     }
     if (SEP_V) {
-      for (int u = threadIdx.x; u < 4 * C::kVch; u += C::kThreads) {
-        const int oct = u / C::kVch, ch = u % C::kVch;
-        u32x4 r[8], c8[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = trow[8 * oct + j];
-          r[j] = row >= 0 ? *(const u32x4*)(vpool + (int64_t)row * v_stride + 8 * ch)
-                          : u32x4{0u, 0u, 0u, 0u};
-        }
-        transpose8x8_to_f16(r, c8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x4*)(vt + (8 * ch + e) * C::kVtRow + 8 * oct) = c8[e];
+      for (int c = 0; c < C::kVC; ++c) {
+        const int row = v_row[c] >= 0 ? tr[v_row[c]] : -1;
+        const u32x4 v = *(const u32x4*)(vpool + (int64_t)max(row, 0) * v_stride + v_off[c]);
+        st.v[c] = row >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < C::kKC; ++c)
+      if (k_row[c] >= 0) *(u32x4*)(ktile + k_row[c] * C::kRow + k_off[c]) = st.k[c];
+    if (SEP_V) {
+#pragma unroll
+      for (int c = 0; c < C::kVC; ++c)
+        if (v_row[c] >= 0) *(u32x4*)(vtile + v_row[c] * C::kVRow + v_off[c]) = st.v[c];
+    }
+  };
 
-    // ---- S^T = K Q^T.  Tile tt, A row m reads token 8*(m/4) + 4*tt + m%4,
-    // so the result lane (head, grp) holds tokens 8*grp + 4*tt + i.
-    f32x4 s[2];
+  f32x4 o[C::kDTH];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int tok = 8 * (col >> 2) + 4 * tt + (col & 3);
-      const uint16_t* krow = ktile + tok * C::kRow + 8 * grp;
+  for (int dt = 0; dt < C::kDTH; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (t_begin < t_end) {
+    load_tile(t_begin);
+    store_tile();
+  }
+  __syncthreads();
+
+  const uint16_t* vsrc = SEP_V ? vtile : ktile;
+  constexpr int kVStride = SEP_V ? C::kVRow : C::kRow;
+  for (int t = t_begin; t < t_end; ++t) {
+    if (t + 1 < t_end) load_tile(t + 1);  // in flight while this tile computes
+    const int32_t* tr = trows + (t - t_begin) * kTile;
+
+    // ---- S^T = K Q^T over this wave's half of the tile: A row m reads
+    // token 8*(m/4) + 4*half + m%4, so the result lane (head, grp) holds
+    // tokens 8*grp + 4*half + i.
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* krow = ktile + (8 * (col >> 2) + 4 * half + (col & 3)) * C::kRow + 8 * grp;
+      constexpr int kDepth = 4;  // LDS operands in flight
+      u32x4 a[kDepth];
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ++ks)
-        s[tt] = mfma16x16x32(as_bf16x8(*(const u32x4*)(krow + 32 * ks)), qf[ks], s[tt]);
+      for (int d = 0; d < kDepth; ++d) a[d] = *(const u32x4*)(krow + 32 * d);
+#pragma unroll
+      for (int ks = 0; ks < C::kKS; ++ks) {
+        const u32x4 x0 = a[ks % kDepth];
+        if (ks + kDepth < C::kKS) a[ks % kDepth] = *(const u32x4*)(krow + 32 * (ks + kDepth));
+        s = mfma16x16x32(as_bf16x8(x0), qf[ks], s);
+      }
     }
 
-    // ---- online softmax (log2 domain); masked tokens contribute nothing
-    float x[8];
+    // ---- online softmax (log2 domain); masked tokens contribute nothing.
+    // The pair agrees on each head's maximum through LDS.  The exponent base
+    // m_run moves only when a maximum exceeds it by more than kRebase, so
+    // weights stay <= 2^kRebase and the O rescale is rare.
+    float x[4];
     float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool valid = trow[8 * grp + j] >= 0;
-      x[j] = valid ? s[j >> 2][j & 3] * scale_log2 : -INFINITY;
-      mt = fmaxf(mt, x[j]);
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = tr[8 * grp + 4 * half + i] >= 0;
+      x[i] = valid ? s[i] * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, x[i]);
     }
     mt = wave_max_xor_16_32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    if (grp == 0) xmax[hb][half][col] = mt;
+    __syncthreads();
+    mt = fmaxf(xmax[hb][0][col], xmax[hb][1][col]);
+    constexpr float kRebase = 8.f;
+    if (m_run == -INFINITY) {
+      m_run = mt;  // first tile with a kept position: O and l are still 0
+    } else if (mt > m_run + kRebase) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      l_run *= alpha;
+      m_run = mt;
+#pragma unroll
+      for (int dt = 0; dt < C::kDTH; ++dt) o[dt] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // P = P_hi + P_lo, both bf16: the pair carries 16 significant bits of
+    // each weight, so the weights add no error worth counting next to the
+    // bf16 output.
+    uint32_t ph[2], pl[2];
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[i] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_use);
+      ph[i >> 1] = pack_bf16x2(p0, p1);
+      pl[i >> 1] = pack_bf16x2(p0 - bf16_lo(ph[i >> 1]), p1 - bf16_hi(ph[i >> 1]));
+    }
+    xp[hb][half][lane] = u32x4{ph[0], ph[1], pl[0], pl[1]};
+    __syncthreads();
+    // k-slot j of the P^T operand is token 8*grp + j: slots 0..3 from the
+    // first half tile, 4..7 from the second.
+    const u32x4 p0 = xp[hb][0][lane], p1 = xp[hb][1][lane];
     float psum = 0.f;
-    uint32_t pk[4];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      pk[j >> 1] = pack_f16x2(__builtin_amdgcn_exp2f(x[j] - m_use),
-                              __builtin_amdgcn_exp2f(x[j + 1] - m_use));
-      // normalise by the weights as they enter the product
-      psum += f16_bits_to_float(pk[j >> 1] & 0xffffu) + f16_bits_to_float(pk[j >> 1] >> 16);
+    for (int w = 0; w < 2; ++w) {
+      psum += bf16_lo(p0[w]) + bf16_hi(p0[w]) + bf16_lo(p0[w + 2]) + bf16_hi(p0[w + 2]);
+      psum += bf16_lo(p1[w]) + bf16_hi(p1[w]) + bf16_lo(p1[w + 2]) + bf16_hi(p1[w + 2]);
     }
-    psum = wave_sum_xor_16_32(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const f16x8 pf = as_f16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+    l_run += wave_sum_xor_16_32(psum);
+    const bf16x8 pf_hi = as_bf16x8(u32x4{p0[0], p0[1], p1[0], p1[1]});
+    const bf16x8 pf_lo = as_bf16x8(u32x4{p0[2], p0[3], p1[2], p1[3]});
 
-    // ---- O^T = alpha * O^T + V^T P^T
-    const uint16_t* vrow = vt + col * C::kVtRow + 8 * grp;
+    // ---- O^T += V^T P^T over this wave's half of the value columns
 #pragma unroll
-    for (int dt = 0; dt < C::kDT; ++dt) {
-      o[dt] *= alpha;
-      o[dt] = mfma16x16x32(as_f16x8(*(const u32x4*)(vrow + 16 * dt * C::kVtRow)), pf, o[dt]);
+    for (int dt = 0; dt < C::kDTH; ++dt) {
+      const bf16x8 va =
+          load_vt_operand(vsrc, kVStride, (D_V / 2) * half + 16 * dt, col, grp);
+      o[dt] = mfma16x16x32(va, pf_hi, o[dt]);
+      o[dt] = mfma16x16x32(va, pf_lo, o[dt]);
     }
+    __syncthreads();
+    if (t + 1 < t_end) store_tile();
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds head `head`, value dims 16*dt + 4*grp + i
+  // ---- epilogue: lane holds head `head`, value dims
+  // (D_V/2)*half + 16*dt + 4*grp + i
   const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse_val = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   if (head < H) {
     if (n_splits == 1) {
-      uint16_t* orow = out + ((int64_t)qi * H + head) * D_V + 4 * grp;
+      uint16_t* orow = out + ((int64_t)qi * H + head) * D_V + (D_V / 2) * half + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) {
+      for (int dt = 0; dt < C::kDTH; ++dt) {
         const uint32_t lo = pack_bf16x2(o[dt][0] * inv_l, o[dt][1] * inv_l);
         const uint32_t hi = pack_bf16x2(o[dt][2] * inv_l, o[dt][3] * inv_l);
         *(uint2*)(orow + 16 * dt) = make_uint2(lo, hi);
       }
-      if (lse && grp == 0) lse[(int64_t)qi * H + head] = lse_val;
+      if (lse && grp == 0 && half == 0) lse[(int64_t)qi * H + head] = lse_val;
     } else {
       const int64_t pidx = ((int64_t)qi * n_splits + split) * H + head;
-      float* prow = part_o + pidx * D_V + 4 * grp;
+      float* prow = part_o + pidx * D_V + (D_V / 2) * half + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt)
-        *(f32x4*)(prow + 16 * dt) = o[dt] * inv_l;
-      if (grp == 0) part_lse[pidx] = lse_val;
+      for (int dt = 0; dt < C::kDTH; ++dt) *(f32x4*)(prow + 16 * dt) = o[dt] * inv_l;
+      if (grp == 0 && half == 0) part_lse[pidx] = lse_val;
     }
   }
 }
@@ -303,17 +401,17 @@ dsa_status_t check_attn_args(const dsa_paged_cache_t* c, const uint16_t* q, cons
   return DSA_OK;
 }
 
-template <int NW, int D_QK, int D_V, bool SEP_V>
+template <int HB, int D_QK, int D_V, bool SEP_V>
 void launch_attn(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q, int H,
                  int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale, uint16_t* out,
                  float* lse, float* part_o, float* part_lse, SplitPlan plan, hipStream_t stream) {
-  const int head_groups = (H + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((sparse_attn_kernel<NW, D_QK, D_V, SEP_V>),
-                     dim3(plan.n_splits, head_groups, n_q), dim3(NW * kWave), 0, stream, c->kv,
-                     c->kv_row_stride, c->v, c->v_row_stride, c->block_table,
-                     c->max_blocks_per_seq, c->block_size, q, idx, K, H, seq_lens, seq, pos0,
-                     plan.tiles_per_split, sm_scale * kLog2e, out, lse, part_o, part_lse,
-                     plan.n_splits);
+  const int head_groups = (H + 16 * HB - 1) / (16 * HB);
+  const int64_t blocks = ((int64_t)n_q + 7) / 8 * 8 * head_groups * plan.n_splits;
+  hipLaunchKernelGGL((sparse_attn_kernel<HB, D_QK, D_V, SEP_V>), dim3((unsigned)blocks),
+                     dim3(2 * HB * kWave), 0, stream, c->kv, c->kv_row_stride, c->v,
+                     c->v_row_stride, c->block_table, c->max_blocks_per_seq, c->block_size, q,
+                     idx, n_q, K, H, head_groups, seq_lens, seq, pos0, plan.tiles_per_split,
+                     sm_scale * kLog2e, out, lse, part_o, part_lse, plan.n_splits);
   if (plan.n_splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel<D_V>, dim3(n_q * H), dim3(128), 0, stream, part_o,
                        part_lse, plan.n_splits, H, out, lse);

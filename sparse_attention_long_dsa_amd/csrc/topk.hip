@@ -150,8 +150,9 @@ __device__ Bucket find_bucket_asc(const uint32_t* hist, int nbins, uint32_t need
 }
 
 // LDS histogram increment with one round of wave aggregation: the lanes that
-// share the first active lane's bin add together (scores that tie or sit in
-// one narrow range would otherwise serialise on a single LDS address).
+// share the first active lane's bin add together with one atomic, the rest
+// add one by one (scores that tie or sit in a narrow range would otherwise
+// serialise on a single LDS address).
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin) {
   const uint64_t act = __ballot(active);
   if (act == 0) return;
@@ -236,10 +237,17 @@ __global__ __launch_bounds__(kThreads) void topk_short_kernel(const float* __res
 
 // ================================================================ long rows
 
+// Per-row counters of the long path.
+struct RowState {
+  uint32_t kept, ncand;  // outright keeps and candidates gathered
+  uint32_t pad[14];
+};
+static_assert(sizeof(RowState) == 64, "RowState is one 64-byte slot");
+
 struct LongWs {
   uint32_t* hist0;   // [n_q][kBins]
   uint32_t* hist1;   // [n_q][kBins]
-  uint32_t* counts;  // [n_q][2]: kept-so-far, candidates
+  RowState* state;   // [n_q]
   int32_t* sel;      // [n_q][K]
   uint2* cand;       // [n_q][ld]: (key, position)
 };
@@ -247,18 +255,17 @@ struct LongWs {
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline size_t long_ws_bytes(int n_q, int64_t ld, int K, LongWs* ws, void* base) {
-  size_t off = 0;
   const size_t h = align_up((size_t)n_q * kBins * 4, 256);
-  const size_t c = align_up((size_t)n_q * 2 * 4, 256);
+  const size_t c = align_up((size_t)n_q * sizeof(RowState), 256);
   const size_t s = align_up((size_t)n_q * K * 4, 256);
   const size_t d = align_up((size_t)n_q * ld * 8, 256);
   if (ws) {
     char* p = (char*)base;
-    ws->hist0 = (uint32_t*)(p + off);
-    ws->hist1 = (uint32_t*)(p + off + h);
-    ws->counts = (uint32_t*)(p + off + 2 * h);
-    ws->sel = (int32_t*)(p + off + 2 * h + c);
-    ws->cand = (uint2*)(p + off + 2 * h + c + s);
+    ws->hist0 = (uint32_t*)p;
+    ws->hist1 = (uint32_t*)(p + h);
+    ws->state = (RowState*)(p + 2 * h);
+    ws->sel = (int32_t*)(p + 2 * h + c);
+    ws->cand = (uint2*)(p + 2 * h + c + s);
   }
   return 2 * h + c + s + d;
 }
@@ -267,6 +274,21 @@ __global__ __launch_bounds__(kThreads) void topk_clear_kernel(uint32_t* p, size_
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < nwords;
        i += (size_t)gridDim.x * kThreads)
     p[i] = 0;
+}
+
+// One 4096-position block of a row: its keys, loaded coalesced.
+struct BlockKeys {
+  uint32_t key[kChunk / kThreads];
+  int s0, s1;
+};
+__device__ __forceinline__ void load_block(const float* src, int s0, int s1, BlockKeys& bk) {
+  bk.s0 = s0;
+  bk.s1 = s1;
+#pragma unroll
+  for (int i = 0; i < kChunk / kThreads; ++i) {
+    const int s = s0 + threadIdx.x + i * kThreads;
+    bk.key[i] = s < s1 ? float_key(src[s]) : 0u;
+  }
 }
 
 // block-wise scoring of the top digit (key bits [31:20])
@@ -279,22 +301,21 @@ __global__ __launch_bounds__(kThreads) void topk_hist0_kernel(const float* __res
   const int n = row_count(n_valid, causal_base, row);
   const int s0 = blockIdx.x * kChunk;
   if (n <= K || s0 >= n) return;
-  const int s1 = min(s0 + kChunk, n);
   for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
+  BlockKeys bk;
+  load_block(scores + (int64_t)row * ld, s0, min(s0 + kChunk, n), bk);
   __syncthreads();
-  const float* src = scores + (int64_t)row * ld;
-  for (int s = s0 + threadIdx.x; s - threadIdx.x < s1; s += kThreads) {
-    const bool ok = s < s1;
-    const uint32_t k = ok ? float_key(src[s]) : 0u;
-    hist_add(hist, ok, k >> 20);
-  }
+#pragma unroll
+  for (int i = 0; i < kChunk / kThreads; ++i)
+    hist_add(hist, s0 + (int)threadIdx.x + i * kThreads < bk.s1, bk.key[i] >> 20);
   __syncthreads();
   uint32_t* g = ws.hist0 + (size_t)row * kBins;
   for (int b = threadIdx.x; b < kBins; b += kThreads)
     if (hist[b]) atomicAdd(&g[b], hist[b]);
 }
 
-// second digit (bits [19:8]) of the keys whose top digit is the threshold's
+// second digit (bits [19:8]) of the keys whose top digit is tau's; every
+// workgroup locates that top digit itself from the merged histogram
 __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(const float* __restrict__ scores,
                                                               int64_t ld,
                                                               const int32_t* __restrict__ n_valid,
@@ -305,16 +326,14 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(const float* __res
   const int n = row_count(n_valid, causal_base, row);
   const int s0 = blockIdx.x * kChunk;
   if (n <= K || s0 >= n) return;
-  const int s1 = min(s0 + kChunk, n);
-  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
   for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
-  __syncthreads();
-  const float* src = scores + (int64_t)row * ld;
-  for (int s = s0 + threadIdx.x; s - threadIdx.x < s1; s += kThreads) {
-    const bool ok = s < s1;
-    const uint32_t k = ok ? float_key(src[s]) : 0u;
-    hist_add(hist, ok && (k >> 20) == b0.bin, (k >> 8) & (kBins - 1));
-  }
+  BlockKeys bk;
+  load_block(scores + (int64_t)row * ld, s0, min(s0 + kChunk, n), bk);
+  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
+#pragma unroll
+  for (int i = 0; i < kChunk / kThreads; ++i)
+    hist_add(hist, s0 + (int)threadIdx.x + i * kThreads < bk.s1 && (bk.key[i] >> 20) == b0.bin,
+             (bk.key[i] >> 8) & (kBins - 1));
   __syncthreads();
   uint32_t* g = ws.hist1 + (size_t)row * kBins;
   for (int b = threadIdx.x; b < kBins; b += kThreads)
@@ -333,81 +352,37 @@ __device__ __forceinline__ uint32_t wave_append(uint32_t* ctr, bool pred) {
   return base + (uint32_t)__popcll(m & lanemask_lt(lane));
 }
 
-// cross-block merge, part 1: keys above the 24-bit threshold prefix are kept
-// outright; keys sharing the prefix are gathered as candidates.
-__global__ __launch_bounds__(kThreads) void topk_collect_kernel(const float* __restrict__ scores,
-                                                                int64_t ld,
-                                                                const int32_t* __restrict__ n_valid,
-                                                                int causal_base, int K, LongWs ws) {
-  __shared__ uint32_t sh[kWaves + 2];
-  const int row = blockIdx.y;
-  const int n = row_count(n_valid, causal_base, row);
-  const int s0 = blockIdx.x * kChunk;
-  if (n <= K || s0 >= n) return;
-  const int s1 = min(s0 + kChunk, n);
-  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
-  const Bucket b1 =
-      find_bucket_desc(ws.hist1 + (size_t)row * kBins, kBins, (uint32_t)K - b0.above, sh);
-  const uint32_t p24 = (b0.bin << 12) | b1.bin;
-  const float* src = scores + (int64_t)row * ld;
-  uint32_t* counts = ws.counts + 2 * (size_t)row;
-  int32_t* sel = ws.sel + (size_t)row * K;
-  uint2* cand = ws.cand + (size_t)row * ld;
-  for (int s = s0 + threadIdx.x; s - threadIdx.x < s1; s += kThreads) {
-    const bool ok = s < s1;
-    const uint32_t k = ok ? float_key(src[s]) : 0u;
-    const bool keep = ok && (k >> 8) > p24;
-    const bool maybe = ok && (k >> 8) == p24;
-    const uint32_t a = wave_append(&counts[0], keep);
-    if (keep) sel[a] = s;
-    const uint32_t c = wave_append(&counts[1], maybe);
-    if (maybe) cand[c] = make_uint2(k, (uint32_t)s);
+// Final step of a row: settle the last 8 key bits and the ties among the
+// candidates, then write the kept positions in ascending order (an LDS
+// bitonic network over <= 2048 positions).
+__device__ void topk_finish_row(int K, uint32_t tau24, uint32_t need1, uint32_t kept,
+                                uint32_t ncand, const int32_t* sel, const uint2* cand_g,
+                                int32_t* out, uint32_t* hist, int32_t* list, uint2* cand_lds,
+                                uint32_t cand_cap, uint32_t* sh, uint32_t* nlist) {
+  const uint2* cand = cand_g;
+  if (ncand <= cand_cap) {  // generic pointer: the passes below read LDS instead of global
+    for (uint32_t c = threadIdx.x; c < ncand; c += kThreads) cand_lds[c] = cand_g[c];
+    cand = cand_lds;
   }
-}
-
-// cross-block merge, part 2 (one workgroup per row): settle the last 8 key
-// bits and the ties among the candidates, then write the kept positions in
-// ascending order (an LDS bitonic network over at most 2048 positions).
-__global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_valid,
-                                                              int causal_base, int K, int64_t ld,
-                                                              LongWs ws,
-                                                              int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[2048];
-  __shared__ int32_t list[2048];
-  __shared__ uint32_t sh[kWaves + 2];
-  __shared__ uint32_t nlist;
-  const int row = blockIdx.x;
-  const int n = row_count(n_valid, causal_base, row);
-  int32_t* out = idx + (int64_t)row * K;
-  if (n <= K) {
-    for (int r = threadIdx.x; r < K; r += kThreads) out[r] = r < n ? r : -1;
-    return;
-  }
-  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
-  const uint32_t need0 = (uint32_t)K - b0.above;
-  const Bucket b1 = find_bucket_desc(ws.hist1 + (size_t)row * kBins, kBins, need0, sh);
-  const uint32_t need1 = need0 - b1.above;  // still to keep among the candidates
-  const uint32_t kept = ws.counts[2 * (size_t)row];
-  const uint32_t ncand = ws.counts[2 * (size_t)row + 1];
-  const uint2* cand = ws.cand + (size_t)row * ld;
-
-  // last digit (bits [7:0]) over the candidates
+  for (uint32_t r = threadIdx.x; r < kept; r += kThreads) list[r] = sel[r];
+  if (threadIdx.x == 0) *nlist = kept;
   for (int b = threadIdx.x; b < 256; b += kThreads) hist[b] = 0;
   __syncthreads();
+
+  // last digit (bits [7:0]) over the candidates
   for (uint32_t c = threadIdx.x; c - threadIdx.x < ncand; c += kThreads) {
     const bool ok = c < ncand;
-    const uint32_t k = ok ? cand[c].x : 0u;
-    hist_add(hist, ok, k & 255u);
+    hist_add(hist, ok, (ok ? cand[c].x : 0u) & 255u);
   }
   __syncthreads();
   const Bucket b2 = find_bucket_desc(hist, 256, need1, sh);
-  const uint32_t tau = (b0.bin << 20) | (b1.bin << 8) | b2.bin;
+  const uint32_t tau = (tau24 << 8) | b2.bin;
   const uint32_t need2 = need1 - b2.above;  // ties at tau to keep, lowest positions first
   const uint32_t nties = hist[b2.bin];
   __syncthreads();
 
-  // lowest `need2` tie positions: position threshold by an ascending radix
-  // search over bits [30:20], [19:10], [9:0]
+  // lowest `need2` tie positions: an ascending radix search over position
+  // bits [30:20], [19:10], [9:0]
   uint32_t pmax = 0xffffffffu;  // keep ties with position <= pmax
   if (need2 < nties) {
     uint32_t prefix = 0, pmask = 0, want = need2;
@@ -432,19 +407,16 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     pmax = prefix;
   }
 
-  // gather the kept positions: the outright ones, then the candidates
-  for (uint32_t r = threadIdx.x; r < kept; r += kThreads) list[r] = ws.sel[(size_t)row * K + r];
-  if (threadIdx.x == 0) nlist = kept;
-  __syncthreads();
+  // add the kept candidates to the outright ones
   for (uint32_t c = threadIdx.x; c - threadIdx.x < ncand; c += kThreads) {
     const bool ok = c < ncand;
     const uint2 e = ok ? cand[c] : make_uint2(0u, 0u);
     const bool take = ok && (e.x > tau || (e.x == tau && e.y <= pmax));
-    const uint32_t a = wave_append(&nlist, take);
+    const uint32_t a = wave_append(nlist, take);
     if (take) list[a] = (int32_t)e.y;
   }
   __syncthreads();
-  // nlist == K here; pad to a power of two and sort ascending
+  // *nlist == K here; pad to a power of two and sort ascending
   int P = 1;
   while (P < K) P <<= 1;
   for (int r = K + threadIdx.x; r < P; r += kThreads) list[r] = 0x7fffffff;
@@ -465,6 +437,78 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     }
   }
   for (int r = threadIdx.x; r < K; r += kThreads) out[r] = list[r];
+}
+
+// cross-block merge, part 1: keys above tau's 24-bit prefix are kept
+// outright and keys sharing it are gathered as candidates; each workgroup
+// counts its own and reserves its output ranges with one atomic per list.
+__global__ __launch_bounds__(kThreads) void topk_collect_kernel(const float* __restrict__ scores,
+                                                                int64_t ld,
+                                                                const int32_t* __restrict__ n_valid,
+                                                                int causal_base, int K, LongWs ws) {
+  __shared__ uint32_t sh[kWaves + 2];
+  __shared__ uint32_t base[2];
+  const int row = blockIdx.y;
+  const int n = row_count(n_valid, causal_base, row);
+  const int s0 = blockIdx.x * kChunk;
+  if (n <= K || s0 >= n) return;
+  BlockKeys bk;
+  load_block(scores + (int64_t)row * ld, s0, min(s0 + kChunk, n), bk);
+  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
+  const Bucket b1 =
+      find_bucket_desc(ws.hist1 + (size_t)row * kBins, kBins, (uint32_t)K - b0.above, sh);
+  const uint32_t p24 = (b0.bin << 12) | b1.bin;
+  uint32_t nk = 0, nm = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk / kThreads; ++i) {
+    const bool ok = s0 + (int)threadIdx.x + i * kThreads < bk.s1;
+    nk += (ok && (bk.key[i] >> 8) > p24) ? 1u : 0u;
+    nm += (ok && (bk.key[i] >> 8) == p24) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t before = block_prefix_excl(nk | (nm << 16), sh, &tot);
+  RowState* st = ws.state + row;
+  if (threadIdx.x == 0) {
+    base[0] = (tot & 0xffffu) ? atomicAdd(&st->kept, tot & 0xffffu) : 0u;
+    base[1] = (tot >> 16) ? atomicAdd(&st->ncand, tot >> 16) : 0u;
+  }
+  __syncthreads();
+  uint32_t ok_at = base[0] + (before & 0xffffu), om_at = base[1] + (before >> 16);
+  int32_t* sel = ws.sel + (size_t)row * K;
+  uint2* cand = ws.cand + (size_t)row * ld;
+#pragma unroll
+  for (int i = 0; i < kChunk / kThreads; ++i) {
+    const int s = s0 + threadIdx.x + i * kThreads;
+    if (s < bk.s1 && (bk.key[i] >> 8) > p24) sel[ok_at++] = s;
+    if (s < bk.s1 && (bk.key[i] >> 8) == p24) cand[om_at++] = make_uint2(bk.key[i], (uint32_t)s);
+  }
+}
+
+// cross-block merge, part 2: one workgroup per row finishes the row.
+__global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_valid,
+                                                              int causal_base, int K, int64_t ld,
+                                                              LongWs ws,
+                                                              int32_t* __restrict__ idx) {
+  constexpr uint32_t kCandCap = 4096;  // candidates cached in LDS
+  __shared__ uint32_t hist[2048];
+  __shared__ int32_t list[2048];
+  __shared__ uint2 cand_lds[kCandCap];
+  __shared__ uint32_t sh[kWaves + 2];
+  __shared__ uint32_t nlist;
+  const int row = blockIdx.x;
+  const int n = row_count(n_valid, causal_base, row);
+  int32_t* out = idx + (int64_t)row * K;
+  if (n <= K) {
+    for (int r = threadIdx.x; r < K; r += kThreads) out[r] = r < n ? r : -1;
+    return;
+  }
+  const Bucket b0 = find_bucket_desc(ws.hist0 + (size_t)row * kBins, kBins, (uint32_t)K, sh);
+  const uint32_t need0 = (uint32_t)K - b0.above;
+  const Bucket b1 = find_bucket_desc(ws.hist1 + (size_t)row * kBins, kBins, need0, sh);
+  const RowState* st = ws.state + row;
+  topk_finish_row(K, (b0.bin << 12) | b1.bin, need0 - b1.above, st->kept, st->ncand,
+                  ws.sel + (size_t)row * K, ws.cand + (size_t)row * ld, out, hist, list,
+                  cand_lds, kCandCap, sh, &nlist);
 }
 
 }  // namespace
@@ -502,9 +546,10 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t ld, int32_t n_q, i
   }
   LongWs ws;
   long_ws_bytes(n_q, ld, K, &ws, workspace);
-  // histograms and counters are contiguous at the start of the workspace
+  // histograms and row states are contiguous at the start of the workspace
   const size_t zero_words = ((char*)ws.sel - (char*)ws.hist0) / 4;
-  hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)std::min<size_t>(1024, (zero_words + 255) / 256)),
+  hipLaunchKernelGGL(topk_clear_kernel,
+                     dim3((unsigned)std::min<size_t>(1024, (zero_words + 255) / 256)),
                      dim3(kThreads), 0, stream, ws.hist0, zero_words);
   const dim3 grid((unsigned)((ld + kChunk - 1) / kChunk), (unsigned)n_q);
   hipLaunchKernelGGL(topk_hist0_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_valid,
