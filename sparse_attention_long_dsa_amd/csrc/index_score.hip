@@ -18,6 +18,8 @@
 // the query stays in registers.  Prefill (item (3): compute bound): each
 // workgroup stages a tile of keys in LDS once and reuses it for a block of
 // queries, so keys are read from HBM once per query block.
+#include <algorithm>
+
 #include "common.h"
 #include "host_util.h"
 
@@ -29,19 +31,18 @@ constexpr int kWaves = kThreads / kWave;
 
 // ---------------------------------------------------------------- decode
 
+// Scores of positions [t0, t1) of sequence b by one workgroup: the query's
+// 64x128 operand sits in registers; the indexer keys stream HBM -> MFMA
+// operand registers with two register buffers, so one round's loads fly
+// while the previous round's MFMAs and epilogue run.
 template <int H_IDX, int D_IDX, int UNROLL>
-__global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
-    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
-    int max_blocks, int bs, const int32_t* __restrict__ seq_lens,
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+__device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx, int64_t k_stride,
+                                              const int32_t* __restrict__ bt_row, int bs,
+                                              const uint16_t* __restrict__ q_row,
+                                              const float* __restrict__ w_row,
+                                              float* __restrict__ out, int t0, int t1) {
   constexpr int HT = (H_IDX + 15) / 16;  // 16-head tiles
   constexpr int KS = D_IDX / 32;         // 32-wide k-steps
-  const int b = blockIdx.y;
-  const int L = seq_lens[b];
-  const int t0 = blockIdx.x * chunk;
-  if (t0 >= L) return;
-  const int t1 = min(t0 + chunk, L);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int col = lane & 15, grp = lane >> 4;
@@ -54,8 +55,7 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < H_IDX)
-        v = *(const u32x4*)(q_idx + ((int64_t)b * H_IDX + head) * D_IDX + 32 * ks + 8 * grp);
+      if (head < H_IDX) v = *(const u32x4*)(q_row + head * D_IDX + 32 * ks + 8 * grp);
       qa[ht][ks] = as_bf16x8(v);
     }
   }
@@ -66,15 +66,10 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int head = 16 * ht + 4 * grp + i;
-      wr[ht][i] = head < H_IDX ? w[(int64_t)b * H_IDX + head] : 0.f;
+      wr[ht][i] = head < H_IDX ? w_row[head] : 0.f;
     }
 
-  const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
-  float* out = scores + (int64_t)b * ld;
   constexpr int kStep = kWaves * 16 * UNROLL;  // tokens per workgroup per round
-
-  // Two register buffers: the loads of the next round fly while this round's
-  // MFMAs and epilogue run.
   auto load = [&](u32x4 (&kb)[UNROLL][KS], int base) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -120,6 +115,82 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
     if (base + 2 * kStep < t1) load(ka, base + 2 * kStep);
     if (base + kStep < t1) compute(kb, base + kStep);
   }
+}
+
+constexpr int kUnroll = 2;      // 16-position groups per wave per register buffer
+constexpr int kFlatMaxSeq = 1024;
+
+// Decode, token-balanced: the batch's positions are laid end to end and
+// each workgroup of a persistent grid takes one equal slice, whatever the
+// ragged lengths; the query is reloaded only where a slice crosses into the
+// next sequence.  Needs n_seq <= kFlatMaxSeq (prefix sums sit in LDS).
+template <int H_IDX, int D_IDX>
+__global__ __launch_bounds__(kThreads, 3) void index_score_decode_flat_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, const int32_t* __restrict__ seq_lens, int n_seq,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    float* __restrict__ scores, int64_t ld) {
+  __shared__ int64_t cum[kFlatMaxSeq + 1];
+  __shared__ int64_t part[kThreads];
+  // exclusive prefix of the lengths: per-thread runs, then a serial pass over
+  // the per-thread totals by one lane
+  const int per = (n_seq + kThreads - 1) / kThreads;
+  const int s0 = threadIdx.x * per, s1 = min(s0 + per, n_seq);
+  int64_t run = 0;
+  for (int i = s0; i < s1; ++i) run += seq_lens[i];
+  part[threadIdx.x] = run;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t acc = 0;
+    for (int t = 0; t < kThreads; ++t) {
+      const int64_t v = part[t];
+      part[t] = acc;
+      acc += v;
+    }
+    cum[n_seq] = acc;
+  }
+  __syncthreads();
+  run = part[threadIdx.x];
+  for (int i = s0; i < s1; ++i) {
+    cum[i] = run;
+    run += seq_lens[i];
+  }
+  __syncthreads();
+  const int64_t total = cum[n_seq];
+  const int64_t lo = total * blockIdx.x / gridDim.x;
+  const int64_t hi = total * (blockIdx.x + 1) / gridDim.x;
+  if (lo >= hi) return;
+  // first sequence whose range ends after lo
+  int b0 = 0, b1 = n_seq - 1;
+  while (b0 < b1) {
+    const int mid = (b0 + b1) / 2;
+    if (cum[mid + 1] <= lo) b0 = mid + 1; else b1 = mid;
+  }
+  for (int b = b0; b < n_seq && cum[b] < hi; ++b) {
+    const int t0 = (int)max<int64_t>(lo - cum[b], 0);
+    const int t1 = (int)min<int64_t>(hi - cum[b], cum[b + 1] - cum[b]);
+    if (t0 >= t1) continue;
+    score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride, block_table + (int64_t)b * max_blocks,
+                                         bs, q_idx + (int64_t)b * H_IDX * D_IDX,
+                                         w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0, t1);
+  }
+}
+
+// Decode, one (sequence, chunk) per workgroup: for batches too wide for the
+// token-balanced kernel.
+template <int H_IDX, int D_IDX>
+__global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+  const int b = blockIdx.y;
+  const int L = seq_lens[b];
+  const int t0 = blockIdx.x * chunk;
+  if (t0 >= L) return;
+  score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride, block_table + (int64_t)b * max_blocks, bs,
+                                       q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX,
+                                       scores + (int64_t)b * ld, t0, min(t0 + chunk, L));
 }
 
 // ---------------------------------------------------------------- prefill
@@ -205,18 +276,37 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
                                 const uint16_t* q_idx, const float* w, int n_q, int seq, int pos0,
                                 float* scores, int64_t ld, hipStream_t stream) {
   if (phase == DSA_DECODE) {
-    // Chunk so that about 4096 workgroups cover n_q * ld positions: about
-    // eight rounds of resident workgroups, so ragged lengths leave a short
-    // tail (each workgroup re-reads its 16 KB query from L2, not HBM).
-    int64_t per = (int64_t)n_q * ld / 4096;
-    int chunk = 1024;  // below this the per-workgroup query load dominates
-    while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
-    const int64_t nchunks = (ld + chunk - 1) / chunk;
-    if (nchunks > 0x7fffffff) return DSA_ERR_SHAPE;
-    hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX, 4>),
-                       dim3((unsigned)nchunks, (unsigned)n_q), dim3(kThreads), 0, stream,
-                       c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
-                       c->block_size, c->seq_lens, q_idx, w, scores, ld, chunk);
+    if (n_q <= kFlatMaxSeq) {
+      // persistent grid: as many workgroups as fit on the device at once
+      static int grid_cache[64] = {0};
+      int dev = 0;
+      (void)hipGetDevice(&dev);
+      int grid = dev < 64 ? grid_cache[dev] : 0;
+      if (grid == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, index_score_decode_flat_kernel<H_IDX, D_IDX>, kThreads, 0) != hipSuccess)
+          return DSA_ERR_HIP;
+        grid = std::max(1, cus * std::max(1, per_cu));
+        if (dev < 64) grid_cache[dev] = grid;
+      }
+      hipLaunchKernelGGL((index_score_decode_flat_kernel<H_IDX, D_IDX>), dim3(grid),
+                         dim3(kThreads), 0, stream, c->k_idx, c->k_idx_row_stride, c->block_table,
+                         c->max_blocks_per_seq, c->block_size, c->seq_lens, n_q, q_idx, w,
+                         scores, ld);
+    } else {
+      // Chunk so that about 4096 workgroups cover n_q * ld positions.
+      int64_t per = (int64_t)n_q * ld / 4096;
+      int chunk = 1024;  // below this the per-workgroup query load dominates
+      while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
+      const int64_t nchunks = (ld + chunk - 1) / chunk;
+      if (nchunks > 0x7fffffff) return DSA_ERR_SHAPE;
+      hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX>),
+                         dim3((unsigned)nchunks, (unsigned)n_q), dim3(kThreads), 0, stream,
+                         c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
+                         c->block_size, c->seq_lens, q_idx, w, scores, ld, chunk);
+    }
   } else {
     constexpr int QB = 64, KB = 128;
     const int64_t nkt = ((int64_t)pos0 + n_q + KB - 1) / KB;
