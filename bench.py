@@ -208,7 +208,7 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cname="c
     """Fold two counter runs of the decode step and two of the plain copy into
     profiles/index_score_decode_traffic.json (HBM bytes per launch).  `cname`
     names the copy kernel (the runtime's device-to-device copy)."""
-    kname = "index_score_decode_kernel"
+    kname = "index_score_decode"
     f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kname)
     w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kname)
     cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", cname)
