@@ -109,7 +109,13 @@ size_t dsa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t K);
  * ordered by lower position first, listed in ascending position order;
  * when n_i < K the row holds 0 .. n_i - 1 followed by -1.
  * -0.0 and +0.0 compare equal; NaN scores are not allowed.
- * n_i must satisfy 0 <= n_i <= ld (not checked: device data). */
+ * n_i must satisfy 0 <= n_i <= ld (not checked: device data).
+ * 1 <= K <= 2048 and ld <= 16777216, else DSA_ERR_SHAPE.  Rows of
+ * ld <= 16384 need no workspace; longer rows need
+ * dsa_topk_workspace_size(n_q, ld, K) bytes (about 8 * n_q * ld), whose
+ * contents need no initialisation and are scratch after the call.  The
+ * result is exact for every input; only the speed depends on the values
+ * (a pruning bound drawn from a strided sample of each long row). */
 dsa_status_t dsa_topk(const float *scores, int64_t ld, int32_t n_q, int32_t K,
                       const int32_t *n_valid, int32_t causal_base, int32_t *idx, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);

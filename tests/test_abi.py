@@ -92,6 +92,7 @@ def test_topk_validation(L):
     assert f(FAKE, 1 << 20, 4, 2048, FAKE, 0, FAKE, FAKE, ws - 1, None) == 4
     assert f(FAKE, 1 << 20, 4, 2048, FAKE, 0, FAKE, FAKE, ws, None) == 5
     assert f(FAKE, 100, 4, 8, None, 96, FAKE, None, 0, None) == 5
+    assert f(FAKE, (1 << 24) + 1, 4, 8, FAKE, 0, FAKE, FAKE, 1 << 40, None) == 2   # ld bound
 
 
 def test_attention_validation(L):

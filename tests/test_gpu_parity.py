@@ -133,7 +133,7 @@ def _topk_case(scores, n_valid, K):
     assert_idx_rows_valid(got, n_valid, K)
 
 
-@pytest.mark.parametrize("ld", [3000, 50000])
+@pytest.mark.parametrize("ld", [3000, 50000, 50001])
 def test_topk_ties_and_special_rows(ld):
     rng = np.random.default_rng(ld)
     rows = [
@@ -150,6 +150,23 @@ def test_topk_ties_and_special_rows(ld):
     n_valid = [ld, ld - 1, ld, 2100, ld // 2, ld, 2049, ld]
     for K in (1, 2048, 777):
         _topk_case(scores, n_valid, K)
+
+
+def test_topk_long_rows_where_pruning_falls_back():
+    """Long rows whose pruned candidate list misleads: a list longer than the
+    in-LDS capacity (two values, heavy ties) and a list shorter than K (high
+    scores placed exactly on the sampled positions - groups of four from
+    floor(4 g n / 8192) - so the sample overrates the bound).  Both must still
+    be exact."""
+    n = 50000
+    rng = np.random.default_rng(7)
+    planted = np.zeros(n)
+    starts = (np.arange(175, dtype=np.int64) * 4 * n) // 8192
+    planted[(starts[:, None] + np.arange(4)).ravel()] = 1.0
+    rows = [rng.integers(0, 2, n).astype(np.float64), planted,
+            planted + rng.integers(0, 3, n) * 1e-3]
+    scores = np.stack(rows).astype(np.float32)
+    _topk_case(scores, [n, n, n], 2048)
 
 
 def test_topk_short_rows_with_fewer_candidates_than_K():
