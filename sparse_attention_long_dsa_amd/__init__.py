@@ -20,7 +20,7 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
-SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip"]
+SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_latent.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # keep packed-fp32 instructions out of the generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -33,6 +33,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPP
 # Per-source extra flags.  The attention kernel keeps its MFMA accumulators
 # in arch VGPRs: with accumulators in AGPRs the compiler copies all of O
 # between the two register files on every tile.
+# the small-head kernel keeps its accumulators in ordinary VGPRs; the
+# latent kernel needs the accumulation registers for its 512 x 32 output
 EXTRA_FLAGS = {"sparse_attn.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 

@@ -1,0 +1,87 @@
+// Internal pieces shared by the two attention kernels (the latent-row
+// kernel and the small MQA kernel): tile size, constants, the split-K plan
+// and the log-sum-exp merge of split partial results.
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace dsa {
+
+constexpr int kTile = 32;  // kept positions per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Split-K plan for decode: enough workgroups to cover the chip about twice.
+struct SplitPlan {
+  int n_splits, tiles_per_split;
+};
+inline SplitPlan plan_splits(int B, int head_groups, int K) {
+  const int tiles = (K + kTile - 1) / kTile;
+  int want = (512 + B * head_groups - 1) / (B * head_groups);
+  want = std::max(1, std::min(want, tiles));
+  const int tps = (tiles + want - 1) / want;
+  return SplitPlan{(tiles + tps - 1) / tps, tps};
+}
+
+// Latent rows: one workgroup per CU; split each query's kept rows so that
+// about 256 workgroups run.
+inline SplitPlan plan_splits_latent(int B, int K) {
+  const int tiles = (K + kTile - 1) / kTile;
+  int want = (256 + B - 1) / B;
+  want = std::max(1, std::min(want, tiles));
+  const int tps = (tiles + want - 1) / want;
+  return SplitPlan{(tiles + tps - 1) / tps, tps};
+}
+
+namespace {
+
+// Log-sum-exp merge of the split-K partial results: one workgroup per
+// (query, head); each thread owns value dims.
+template <int D_V>
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           int n_splits, int H,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const int qh = blockIdx.x;  // qi * H + head
+  const int qi = qh / H, head = qh % H;
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s)
+    m = fmaxf(m, part_lse[((int64_t)qi * n_splits + s) * H + head]);
+  float wsum = 0.f;
+  float acc[D_V / 128 > 0 ? D_V / 128 : 1] = {};
+  constexpr int kPer = D_V / 128 > 0 ? D_V / 128 : 1;
+  for (int s = 0; s < n_splits; ++s) {
+    const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
+    const float l = part_lse[p];
+    const float wgt = l == -INFINITY ? 0.f : __expf(l - m);
+    wsum += wgt;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int d = threadIdx.x + 128 * e;
+      if (d < D_V) acc[e] += wgt * part_o[p * D_V + d];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int d = threadIdx.x + 128 * e;
+    if (d < D_V) out[(int64_t)qh * D_V + d] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+  }
+  if (lse && threadIdx.x == 0) lse[qh] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
+}  // namespace
+
+// Launches the latent-row kernel (128 heads on a 576-wide row, V = its
+// first 512 columns), and the split merge when plan.n_splits > 1.
+void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
+                   int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
+                   uint16_t* out, float* lse, float* part_o, float* part_lse, SplitPlan plan,
+                   hipStream_t stream);
+
+}  // namespace dsa

@@ -4,10 +4,14 @@
 // exact attention over the Top-K positions, item (2) paged layout with an
 // index table, item (3) separate prefill and decode paths).
 //
+// This file holds the kernel for small multi-query heads (heads sharing one
+// K/V head with separate K and V pools, d = 64) and the entry points of both
+// attention calls; rows of the 576-wide latent shape go to the kernel in
+// sparse_attn_latent.hip.
+//
 // One workgroup takes one query and a group of 16*NW heads; all heads share
-// one K/V head (MQA, or the shared latent row where V is the first d_v
-// columns of K), so each gathered tile in LDS serves every head of the
-// group.  Per tile of 32 kept positions:
+// one K/V head, so each gathered tile in LDS serves every head of the group.
+// Per tile of 32 kept positions:
 //   gather:  32 rows go from HBM into an LDS K tile [token][d_qk] (bf16);
 //            the loads of tile t+1 are in flight in registers while tile t
 //            computes;
@@ -16,8 +20,7 @@
 //                 statistics need only two cross-lane steps);
 //   online softmax in the log2 domain with fp32 statistics;
 //   O^T += V^T P^T on MFMA (A = V^T read straight from the row-major tile
-//                 with the gfx950 LDS transpose load - for the latent row V
-//                 is the first d_v columns of the K tile - and B = P^T
+//                 with the gfx950 LDS transpose load, B = P^T
 //                 straight from the S^T accumulators, so P never leaves
 //                 registers; O^T's lane layout matches the per-head
 //                 statistics, so rescaling needs no data movement).
@@ -29,17 +32,11 @@
 // kernel; prefill has enough queries to fill the chip without splitting.
 #include <algorithm>
 
-#include "common.h"
+#include "attn_common.h"
 #include "host_util.h"
 
 namespace dsa {
 namespace {
-
-constexpr int kTile = 32;  // kept positions per LDS tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // A 16x32 bf16 operand of V^T (rows: 16 value columns from dv0, k: tokens
 // 8*grp .. 8*grp+7) read from a row-major [token][column] LDS tile with two
@@ -330,54 +327,6 @@ __global__ __launch_bounds__(2 * HB * kWave) void sparse_attn_kernel(
   }
 }
 
-// Log-sum-exp merge of the split-K partial results: one workgroup per
-// (query, head); each thread owns value dims.
-template <int D_V>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
-                                                           int n_splits, int H,
-                                                           uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  const int qh = blockIdx.x;  // qi * H + head
-  const int qi = qh / H, head = qh % H;
-  float m = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    m = fmaxf(m, part_lse[((int64_t)qi * n_splits + s) * H + head]);
-  float wsum = 0.f;
-  float acc[D_V / 128 > 0 ? D_V / 128 : 1] = {};
-  constexpr int kPer = D_V / 128 > 0 ? D_V / 128 : 1;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
-    const float l = part_lse[p];
-    const float wgt = l == -INFINITY ? 0.f : __expf(l - m);
-    wsum += wgt;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int d = threadIdx.x + 128 * e;
-      if (d < D_V) acc[e] += wgt * part_o[p * D_V + d];
-    }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int d = threadIdx.x + 128 * e;
-    if (d < D_V) out[(int64_t)qh * D_V + d] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
-  }
-  if (lse && threadIdx.x == 0) lse[qh] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
-}
-
-// Split-K plan for decode: enough workgroups to cover the chip about twice.
-struct SplitPlan {
-  int n_splits, tiles_per_split;
-};
-inline SplitPlan plan_splits(int B, int head_groups, int K) {
-  const int tiles = (K + kTile - 1) / kTile;
-  int want = (512 + B * head_groups - 1) / (B * head_groups);
-  want = std::max(1, std::min(want, tiles));
-  const int tps = (tiles + want - 1) / want;
-  return SplitPlan{(tiles + tps - 1) / tps, tps};
-}
-
 enum Family { kLatent, kSmall, kNone };
 
 Family family_of(const dsa_paged_cache_t* c, int H) {
@@ -419,6 +368,11 @@ void launch_attn(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* i
 
 int head_groups_of(int H) { return H == 128 ? 2 : 1; }
 
+// Split plan of the decode call (also what sizes its workspace).
+SplitPlan decode_plan(int B, int H, int K, int d_v) {
+  return (H == 128 && d_v == 512) ? plan_splits_latent(B, K) : plan_splits(B, head_groups_of(H), K);
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -426,7 +380,7 @@ extern "C" size_t dsa_sparse_attn_decode_workspace_size(int32_t B, int32_t H, in
                                                          int32_t d_v) {
   using namespace dsa;
   if (B < 1 || H < 1 || K < 1 || d_v < 1) return 0;
-  const SplitPlan p = plan_splits(B, head_groups_of(H), K);
+  const SplitPlan p = decode_plan(B, H, K, d_v);
   if (p.n_splits == 1) return 0;
   const size_t o = (size_t)B * p.n_splits * H * d_v * 4;
   return (o + 255) / 256 * 256 + (size_t)B * p.n_splits * H * 4;
@@ -447,14 +401,14 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   st = check_device();
   if (st != DSA_OK) return st;
-  const SplitPlan plan = plan_splits(B, head_groups_of(H), K);
+  const SplitPlan plan = decode_plan(B, H, K, cache->d_v);
   float* part_o = (float*)workspace;
   float* part_lse = need ? (float*)((char*)workspace +
                                     ((size_t)B * plan.n_splits * H * cache->d_v * 4 + 255) / 256 * 256)
                          : nullptr;
   if (fam == kLatent)
-    launch_attn<4, 576, 512, false>(cache, q, idx, B, H, K, cache->seq_lens, 0, 0, sm_scale, out,
-                                    lse, part_o, part_lse, plan, stream);
+    launch_latent(cache, q, idx, B, K, cache->seq_lens, 0, 0, sm_scale, out, lse, part_o,
+                  part_lse, plan, stream);
   else
     launch_attn<1, 64, 64, true>(cache, q, idx, B, H, K, cache->seq_lens, 0, 0, sm_scale, out,
                                  lse, part_o, part_lse, plan, stream);
@@ -477,8 +431,8 @@ extern "C" dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t* cache,
   if (st != DSA_OK) return st;
   const SplitPlan one{1, (K + kTile - 1) / kTile};
   if (fam == kLatent)
-    launch_attn<4, 576, 512, false>(cache, q, idx, T, H, K, nullptr, seq, pos0, sm_scale, out,
-                                    lse, nullptr, nullptr, one, stream);
+    launch_latent(cache, q, idx, T, K, nullptr, seq, pos0, sm_scale, out, lse, nullptr, nullptr,
+                  one, stream);
   else
     launch_attn<1, 64, 64, true>(cache, q, idx, T, H, K, nullptr, seq, pos0, sm_scale, out, lse,
                                  nullptr, nullptr, one, stream);
