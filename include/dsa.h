@@ -36,7 +36,8 @@
  *       attention (H, d_qk, d_v) = (128, 576, 512) with V the first 512
  *                 columns of each K row (cache->v == NULL), or (8, 64, 64)
  *                 with a separate V pool;
- *       1 <= K <= 2048; any block_size >= 1; any lengths.
+ *       1 <= K <= 2048; any lengths; block_size a multiple of 16 for
+ *       dsa_index_score, any block_size >= 1 for the other calls.
  */
 #ifndef DSA_H
 #define DSA_H

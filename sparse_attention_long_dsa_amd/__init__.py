@@ -275,6 +275,7 @@ class DecodeStep:
         import torch
 
         self.cache, self.K = cache, K
+        ld = (ld + 63) // 64 * 64  # aligned score rows: 16-byte loads in Top-K
         self.scores = torch.empty((B, ld), dtype=torch.float32, device=device)
         self.idx = torch.empty((B, K), dtype=torch.int32, device=device)
         self.out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=device)
@@ -300,7 +301,7 @@ class PrefillStep:
         import torch
 
         self.cache, self.K, self.T, self.pos0 = cache, K, T, pos0
-        ld = pos0 + T
+        ld = (pos0 + T + 63) // 64 * 64  # aligned score rows
         self.scores = torch.empty((T, ld), dtype=torch.float32, device=device)
         self.idx = torch.empty((T, K), dtype=torch.int32, device=device)
         self.out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=device)

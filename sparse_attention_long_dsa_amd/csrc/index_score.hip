@@ -70,18 +70,24 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
     }
 
   constexpr int kStep = kWaves * 16 * UNROLL;  // tokens per workgroup per round
+  // Rounds start on a multiple of 16, so a 16-position group never straddles
+  // a cache block (block sizes are multiples of 16) and its block-table
+  // entry is one scalar load.  Scalar loads wait on their own counter, so
+  // looking up the next round's blocks never waits for key loads in flight.
+  // Loads carry no branches (so the compiler can keep a whole buffer of them
+  // in flight): a group starting at or past t1 reads the last group again,
+  // and positions of a group outside [t0, t1) are read from the same
+  // physical block; none of these are written.
+  const int a0 = t0 & ~15;
+  const int g_last = (t1 - 1) & ~15;
   auto load = [&](u32x4 (&kb)[UNROLL][KS], int base) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int tok = base + 16 * u + col;
-      if (tok < t1) {
-        const uint16_t* row = k_idx + paged_row(bt_row, bs, tok) * k_stride + 8 * grp;
+      const int g0 = __builtin_amdgcn_readfirstlane(min(base + 16 * u, g_last));
+      const int64_t phys = bt_row[g0 / bs];
+      const uint16_t* row = k_idx + (phys * bs + g0 % bs + col) * k_stride + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb[u][ks] = *(const u32x4*)(row + 32 * ks);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb[u][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int ks = 0; ks < KS; ++ks) kb[u][ks] = *(const u32x4*)(row + 32 * ks);
     }
   };
   auto compute = [&](const u32x4 (&kb)[UNROLL][KS], int base) {
@@ -102,18 +108,22 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
         for (int i = 0; i < 4; ++i) s += wr[ht][i] * fmaxf(acc[ht][i], 0.f);
       s = wave_sum_xor_16_32(s);
       const int tok = base + 16 * u + col;
-      if (grp == 0 && tok < t1) out[tok] = s;
+      if (grp == 0 && tok >= t0 && tok < t1) out[tok] = s;
     }
   };
 
+  // The loop body has no branches either (a round past t1 re-reads the
+  // last group and writes nothing), so the compiler's load counting stays
+  // exact and each compute waits only for its own buffer.
   u32x4 ka[UNROLL][KS], kb[UNROLL][KS];
-  int base = t0 + wave * 16 * UNROLL;
-  if (base < t1) load(ka, base);
+  int base = a0 + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * 16 * UNROLL;
+  if (base >= t1) return;
+  load(ka, base);
   for (; base < t1; base += 2 * kStep) {
-    if (base + kStep < t1) load(kb, base + kStep);
+    load(kb, base + kStep);
     compute(ka, base);
-    if (base + 2 * kStep < t1) load(ka, base + 2 * kStep);
-    if (base + kStep < t1) compute(kb, base + kStep);
+    load(ka, base + 2 * kStep);
+    compute(kb, base + kStep);
   }
 }
 
@@ -346,6 +356,7 @@ extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phas
   const bool small = H_idx == 4 && cache->d_idx == 32;
   if (!big && !small) return DSA_ERR_UNSUPPORTED;
   if (cache->k_idx_row_stride % 8 != 0) return DSA_ERR_UNSUPPORTED;  // 16-byte row alignment
+  if (cache->block_size % 16 != 0) return DSA_ERR_UNSUPPORTED;        // 16-position groups
   st = check_device();
   if (st != DSA_OK) return st;
   if (big)
