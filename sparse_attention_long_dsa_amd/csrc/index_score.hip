@@ -127,7 +127,7 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
   }
 }
 
-constexpr int kUnroll = 2;      // 16-position groups per wave per register buffer
+constexpr int kUnroll = 4;      // 16-position groups per wave per register buffer
 constexpr int kFlatMaxSeq = 1024;
 
 // Decode, token-balanced: the batch's positions are laid end to end and
@@ -135,7 +135,7 @@ constexpr int kFlatMaxSeq = 1024;
 // ragged lengths; the query is reloaded only where a slice crosses into the
 // next sequence.  Needs n_seq <= kFlatMaxSeq (prefix sums sit in LDS).
 template <int H_IDX, int D_IDX>
-__global__ __launch_bounds__(kThreads, 3) void index_score_decode_flat_kernel(
+__global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, const int32_t* __restrict__ seq_lens, int n_seq,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
