@@ -11,38 +11,50 @@ namespace {
 // ===================================================== latent rows (MLA shape)
 //
 // 128 heads share one 576-wide row (512 value/latent + 64 rope columns, V =
-// the first 512).  One workgroup takes one query and all 128 heads: four
-// waves, one per SIMD, each owning 32 heads, so every row a tile brings
-// into LDS is read once per wave for S and once per wave for P V, and the
-// kernel is bound by the matrix cores rather than by LDS.
+// the first 512).  One workgroup takes one query and all 128 heads with
+// four waves, one per SIMD.  The two products split the work differently:
+//   S^T = K Q^T by heads: wave w owns heads 32 w .. 32 w + 31 (its q stays
+//        in registers for the whole kernel), MFMA 32x32x16 bf16 with the K
+//        rows as the A operand read from LDS;
+//   O^T += V^T P^T by value columns: wave w owns columns 128 w .. + 127 for
+//        all 128 heads, so each V^T operand (the slow LDS transpose read) is
+//        read by one wave only and serves 4 head blocks.  P (bf16 hi + lo,
+//        16 significant bits of each weight) goes through a small LDS
+//        buffer from the wave that computed it to all four.
+// Softmax statistics stay with the head owner; the exponent base of a head
+// is its maximum over the first tile and never moves, so O^T (128 heads x
+// 128 columns fp32 per wave, in the accumulation registers) is never
+// rescaled.  A block whose later logits pass that base by more than 2^64 in
+// weight runs its tiles again with the true maximum as the base.
 //
-// Per tile of 32 kept rows:
-//   gather:  the rows go from HBM straight into LDS with the gfx950 direct
-//            global->LDS load (16 bytes a lane, no registers); the next
-//            tile's loads are in flight while this tile computes (two LDS
-//            buffers);
-//   S^T = K Q^T on MFMA 32x32x16 bf16 (A = K rows from LDS, B = q held in
-//            registers for the whole kernel); the A rows are read in a
-//            permuted order so that each result lane holds one head and 16
-//            tokens laid out exactly as the P^T operand of P V needs them;
-//   online softmax in the log2 domain, per head in one lane pair;
-//   O^T += V^T P^T on MFMA 32x32x16 (A = V^T read with the LDS transpose
-//            load from the same tile, B = P^T straight from registers, as
-//            bf16 hi + lo).  O^T (512 x 32 fp32 per wave) lives in the
-//            accumulation registers.
+// Tiles of 32 kept rows go from HBM straight into LDS (gfx950 direct
+// global->LDS loads, no registers), one tile ahead.  Iteration t computes
+// S(t) and the softmax of tile t, then O += V P for tile t - 1: three tile
+// buffers (t - 1 for V, t for K, t + 1 loading) and two P buffers, one
+// barrier per tile.
 namespace latent {
 
 constexpr int kDqk = 576, kDv = 512, kHeads = 128;
 constexpr int kWaves = 4, kThreads = kWaves * kWave;
-constexpr int kRowSlots = kDqk / 8 + 1;             // 72 16-byte chunks + 1 pad slot (LDS banks)
-constexpr int kRowElems = kRowSlots * 8;            // LDS row stride (elements)
-constexpr int kTileSlots = kTile * kRowSlots;       // 2336
-constexpr int kLoadBlocks = (kTileSlots + kWave - 1) / kWave;  // 37 wave loads hold a tile
-constexpr int kWaveBlocks = (kLoadBlocks + kWaves - 1) / kWaves;  // loads per wave (all equal)
-constexpr int kBufSlots = kWaveBlocks * kWaves * kWave;  // slots past the tile take junk
-constexpr int kBufs = 3;                            // tiles t, t + 1, t + 2 in flight
+// LDS tile: the 512 latent (value) columns of each row at a stride of 67
+// 16-byte slots (the 16 rows an A-operand read touches land in 16 different
+// bank groups, and the 4 rows of a transposed V read in disjoint ones),
+// followed by the 64 rope columns of all 32 rows in 8-slot rows whose chunk
+// index is XOR-swizzled by bits 1..3 of the row.
+constexpr int kLatBytes = kDv * 2;                  // 1024
+constexpr int kRowBytes = kLatBytes + 48;           // 1072
+constexpr int kRowElems = kRowBytes / 2;            // LDS row stride (elements)
+constexpr int kRopeChunks = (kDqk - kDv) / 8;       // 8
+constexpr int kLatRegion = kTile * kRowBytes;       // bytes
+constexpr int kBufBytes = kLatRegion + kTile * kRopeChunks * 16;
+constexpr int kRopeElems = kLatRegion / 2;          // element offset of the rope rows
+constexpr int kBufs = 3;
 constexpr int kKS = kDqk / 16;                      // k-steps of S
-constexpr int kDVB = kDv / 32;                      // 32-wide value blocks
+constexpr int kKSLat = kDv / 16;                    // k-steps over the latent columns
+constexpr int kDvWave = kDv / kWaves;               // value columns per wave
+constexpr int kDVB = kDvWave / 32;                  // 32-wide value blocks per wave
+constexpr int kHB = kHeads / 32;                    // 32-head blocks
+constexpr int kPElems = kHeads * kTile;             // one P plane (bf16)
 constexpr int kMaxTiles = 2048 / kTile;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -50,7 +62,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Direct global -> LDS load of 16 bytes a lane (lane l fills LDS bytes
 // lds + 16 l .. + 15), written out so that the compiler does not track it:
 // it would otherwise wait for every such load in flight before each LDS read,
-// which serialises the loads of the tiles ahead with the current tile's
+// which serialises the loads of the next tile with the current tile's
 // products.  Completion is awaited explicitly (s_waitcnt vmcnt) before the
 // barrier that hands a tile to its readers.  M0 is saved and restored.
 __device__ __forceinline__ void global_to_lds16(const void* src, uint32_t lds) {
@@ -62,6 +74,19 @@ __device__ __forceinline__ void global_to_lds16(const void* src, uint32_t lds) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds)
+      : "memory");
+}
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane
+// 32-bit byte offset (no vector address arithmetic).
+__device__ __forceinline__ void global_to_lds16_s(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
 
@@ -85,9 +110,6 @@ __device__ __forceinline__ void mfma32_vgpr_first(f32x16& acc, bf16x8 a, bf16x8 
 __device__ __forceinline__ void mfma_result_fence(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
-__device__ __forceinline__ void mfma_result_fence(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
-}
 
 // Token held in accumulator slot v by a lane of half h (= lane / 32):
 // 8 h + (v % 8) for v < 8, 16 + 8 h + (v % 8) for v >= 8.  Accumulator row
@@ -99,16 +121,23 @@ __device__ __forceinline__ int perm_row(int m) {
   return 16 * (b >> 1) + 8 * h + 4 * (b & 1) + i;
 }
 
-// A operand of O^T += V^T P^T for value block dvb and token half ks: lane l
-// holds value column 32 dvb + l % 32 and tokens 16 ks + 8 (l / 32) .. + 7.
-// Within each 16-lane group, lane i names V[t0 + i / 4][c0 + 4 (i % 4) ..]
-// and the transpose load hands lane j the column c0 + j of 4 tokens.
-__device__ __forceinline__ bf16x8 load_vt32(const uint16_t* tile, int dvb, int ks, int lane) {
+// P buffer layout: plane (hi, lo) x head x 4 chunks of 8 tokens; the chunk
+// index is XOR-swizzled with bits 2..3 of the head so that 16 lanes reading
+// 16 heads at one chunk hit 16 different bank groups.
+__device__ __forceinline__ int p_offset(int plane, int head, int chunk) {
+  return plane * kPElems + head * kTile + 8 * (chunk ^ ((head >> 2) & 3));
+}
+
+// A operand of O^T += V^T P^T for value columns c0 .. c0 + 31 and token
+// half ks: lane l holds column c0 + l % 32 and tokens 16 ks + 8 (l / 32)
+// .. + 7.  Within each 16-lane group, lane i names V[t0 + i / 4][c + 4 (i %
+// 4) ..] and the transpose load hands lane j the column c + j of 4 tokens.
+__device__ __forceinline__ bf16x8 load_vt32(const uint16_t* tile, int c0, int ks, int lane) {
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   const int g = lane >> 4, i = lane & 15;
-  const int c0 = 32 * dvb + 16 * (g & 1);
+  const int c = c0 + 16 * (g & 1);
   const int t0 = 16 * ks + 8 * (g >> 1);
-  const uint16_t* p0 = tile + (t0 + (i >> 2)) * kRowElems + c0 + 4 * (i & 3);
+  const uint16_t* p0 = tile + (t0 + (i >> 2)) * kRowElems + c + 4 * (i & 3);
   const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
   const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * kRowElems));
   const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
@@ -121,8 +150,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     int n_q, int K, const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0,
     int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[kBufs][kBufSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[kBufs][kBufBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][2 * kPElems];
   __shared__ int32_t trows[kMaxTiles * kTile];
+  __shared__ float head_l[kHeads], head_lse[kHeads];
 
   // blocks of one query share an XCD (same block id modulo 8)
   const int b = blockIdx.x;
@@ -139,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar
   const int half = lane >> 5;
-  const int head = 32 * wave + (lane & 31);  // this lane's head (B operand column, O^T column)
+  const int head = 32 * wave + (lane & 31);  // head whose S row and statistics this lane holds
 
   const int n_tiles = (count + kTile - 1) / kTile;
   const int t_begin = split * tiles_per_split;
@@ -159,55 +190,64 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     const uint16_t* qrow = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 16 * ks));
+    // Consume q here, so that the compiler waits for these loads before the
+    // tile loop.  Otherwise it counts them as possibly in flight inside the
+    // loop and its waits there (which also cover the direct-to-LDS tile
+    // loads it does not see) would drain the next tile's loads every tile.
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
   __syncthreads();
 
-  // Wave w issues the tile's 16-byte slots 64 b + lane for b = w, w + 4, ...
-  // (its i-th block is b = w + 4 i; every wave issues kWaveBlocks, so the
-  // per-wave count of loads in flight is known).  Slot s is chunk s % 73 of
-  // tile row s / 73; the pad chunk and the tail slots past the tile load a
-  // valid chunk that nothing reads.  The blocks of a tile are issued one by
-  // one between the S products of the tile two places earlier.
+  // Loads of a tile: wave w brings rows 8 w .. 8 w + 7, one wave load per
+  // row for the 512 latent columns (lane l: bytes 16 l .. of the row, the
+  // row address is wave-uniform and lives in SGPRs) and one wave load for the
+  // rope columns of all 8 rows (lane l: row 8 w + l / 8, the chunk that the
+  // swizzle puts at rope slot 64 w + l).
+  constexpr int kWaveRows = kTile / kWaves;       // 8
+  constexpr int kWaveBlocks = kWaveRows + 1;      // 9 wave loads a tile
   const int32_t* ld_tr = trows;
-  int ld_buf = 0, ld_r = 0, ld_c = 0;
+  int ld_buf = 0, ld_next = 0, ld_rope = 0;
+  const int rope_row = kWaveRows * wave + (lane >> 3);
+  const uint32_t rope_col = kLatBytes + 16u * (uint32_t)((lane & 7) ^ ((rope_row >> 1) & 7));
   auto load_begin = [&](int t, int buf) {
-    ld_tr = trows + (t - t_begin) * kTile;
+    ld_tr = trows + (t - t_begin) * kTile + kWaveRows * wave;
     ld_buf = buf;
-    const int s0 = kWave * wave + lane;
-    ld_r = s0 / kRowSlots;
-    ld_c = s0 - ld_r * kRowSlots;
+    ld_next = ld_tr[0];
+    ld_rope = ld_tr[lane >> 3];
   };
   const uint32_t tiles_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tiles;
   const uint64_t row_bytes = (uint64_t)kv_stride * 2;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto load_block = [&](int i) {
-    const int blk = wave + kWaves * i;
-    const int rr = ld_r < kTile ? ld_r : 0;
-    const int cc = ld_c < kDqk / 8 ? ld_c : 0;
-    const char* src = (const char*)kv + (uint64_t)(uint32_t)ld_tr[rr] * row_bytes + 16 * cc;
-    global_to_lds16(src, tiles_lds + (uint32_t)(ld_buf * kBufSlots + kWave * blk) * 16u);
-    // this wave's next block is 256 slots on
-    constexpr int kStepRows = kWaves * kWave / kRowSlots;
-    constexpr int kStepSlots = kWaves * kWave % kRowSlots;
-    ld_c += kStepSlots;
-    ld_r += kStepRows;
-    if (ld_c >= kRowSlots) {
-      ld_c -= kRowSlots;
-      ++ld_r;
+    const uint32_t buf_lds = tiles_lds + (uint32_t)(ld_buf * kBufBytes);
+    if (i < kWaveRows) {
+      const int row = __builtin_amdgcn_readfirstlane(ld_next);
+      if (i + 1 < kWaveRows) ld_next = ld_tr[i + 1];
+      const char* src = (const char*)kv + (uint64_t)(uint32_t)row * row_bytes;
+      global_to_lds16_s(src, lane16, buf_lds + (uint32_t)((kWaveRows * wave + i) * kRowBytes));
+    } else {
+      const char* src = (const char*)kv + (uint64_t)(uint32_t)ld_rope * row_bytes + rope_col;
+      global_to_lds16(src, buf_lds + (uint32_t)(kLatRegion + kWave * 16 * wave));
     }
   };
 
   // A operand rows of S^T: this lane reads tile row perm(lane % 32), dims
   // 16 ks + 8 half .. + 7
-  const int a_off = perm_row(lane & 31) * kRowElems + 8 * half;
+  const int a_row = perm_row(lane & 31);
+  const int a_off = a_row * kRowElems + 8 * half;
+  // rope columns of that row: chunk 2 kc + half sits at slot
+  // 8 row + ((2 kc + half) ^ x), x = bits 1..3 of the row; the XOR with 2 kc
+  // only touches bits 4..5 of the element offset
+  const int a_rope = kRopeElems + 64 * a_row + 8 * (half ^ ((a_row >> 1) & 7));
+  const int c_wave = kDvWave * wave;  // first value column of this wave
+  auto a_operand = [&](const uint16_t* tile, int ks) {
+    const int off = ks < kKSLat ? a_off + 16 * ks : a_rope ^ (16 * (ks - kKSLat));
+    return as_bf16x8(*(const u32x4*)(tile + off));
+  };
 
-  // Softmax base: the exponent base of a head is its maximum over the first
-  // tile and is never moved, so O^T is never rescaled inside the loop (its
-  // 256 registers stay in the accumulation file).  Later tiles may give
-  // weights above 1; fp32 and bf16 hold them exactly as well up to 2^kMaxExp.
-  // If any head passes that, the block runs the tiles a second time with the
-  // base set to the true maximum (rare: a logit 44 above the first tile's).
   constexpr float kMaxExp = 64.f;
-  f32x16 o[kDVB];
+  f32x16 o[kHB][kDVB];
   float m_base = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
   bool redo = false;
 #pragma unroll 1
@@ -217,140 +257,157 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       m_base = m_seen;
     }
 #pragma unroll
-    for (int d = 0; d < kDVB; ++d) o[d] = f32x16{};
+    for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+      for (int d = 0; d < kDVB; ++d) o[hb][d] = f32x16{};
     l_run = 0.f;
+    if (t_begin < t_end) {
+      load_begin(t_begin, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (t_begin + j < t_end) {
-        load_begin(t_begin + j, j);
-#pragma unroll
-        for (int i = 0; i < kWaveBlocks; ++i) load_block(i);
-      }
+      for (int i = 0; i < kWaveBlocks; ++i) load_block(i);
     }
 
-    for (int t = t_begin; t < t_end; ++t) {
-      const int buf = (t - t_begin) % kBufs;
-      // this tile's rows have landed (the next tile's kWaveBlocks loads may
-      // still fly) ...
-      if (t + 1 < t_end)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaveBlocks) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // ... for every wave, and tile t - 1's buffer is free
-      const bool next = t + 2 < t_end;
-      if (next) load_begin(t + 2, (buf + 2) % kBufs);
-      const uint16_t* tile = tiles[buf];
+    // iteration t: S and softmax of tile t (t < t_end), then O += V P of
+    // tile t - 1 (t > t_begin)
+    for (int t = t_begin; t <= t_end; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t has landed (this wave's part)
+      __syncthreads();  // ... all of it; P(t - 1) is written; tile t - 2 and P(t - 2) are free
+      const bool have_s = t < t_end;
+      const bool next = t + 1 < t_end;
+      if (next) load_begin(t + 1, (t + 1 - t_begin) % kBufs);
 
-      // ---- S^T = K Q^T.  With one wave per SIMD nothing else hides LDS
-      // latency, so the A operands are read kDepthS k-steps ahead into a
-      // ring (a slot is refilled two products after its last use).
-      constexpr int kDepthS = 4, kRingS = kDepthS + 2;
-      f32x16 s, s_odd;
-      bf16x8 ar[kRingS];
+      if (have_s) {
+        const uint16_t* tile = tiles[(t - t_begin) % kBufs];
+        // ---- S^T = K Q^T; the A operands are read kDepthS k-steps ahead
+        constexpr int kDepthS = 2, kRingS = kDepthS + 2;
+        f32x16 s;
+        bf16x8 ar[kRingS];
 #pragma unroll
-      for (int j = 0; j < kDepthS; ++j) ar[j] = as_bf16x8(*(const u32x4*)(tile + a_off + 16 * j));
+        for (int jj = 0; jj < kDepthS; ++jj) ar[jj] = a_operand(tile, jj);
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        f32x16& acc = (ks & 1) ? s_odd : s;
-        if (ks < 2)
-          mfma32_vgpr_first(acc, ar[ks], qf[ks]);
-        else
-          mfma32_vgpr(acc, ar[ks % kRingS], qf[ks]);
-        if (ks + kDepthS < kKS)
-          ar[(ks + kDepthS) % kRingS] = as_bf16x8(*(const u32x4*)(tile + a_off + 16 * (ks + kDepthS)));
-        if (next && ks % 3 == 1 && ks / 3 < kWaveBlocks) load_block(ks / 3);
-      }
-      mfma_result_fence(s, s_odd);
-      s += s_odd;
+        for (int ks = 0; ks < kKS; ++ks) {
+          if (ks == 0)
+            mfma32_vgpr_first(s, ar[0], qf[0]);
+          else
+            mfma32_vgpr(s, ar[ks % kRingS], qf[ks]);
+          if (ks + kDepthS < kKS)
+            ar[(ks + kDepthS) % kRingS] = a_operand(tile, ks + kDepthS);
+          if (next && ks < kWaveBlocks) load_block(ks);
+        }
+        mfma_result_fence(s);
 
-      // ---- softmax weights, log2 domain; masked tokens (only in a range's
-      // last tile) get weight 0
-      const int g0 = t * kTile;
-      const bool full = g0 + kTile <= count;
-      float sv[16];
-      float mt = -INFINITY;
+        // ---- softmax weights, log2 domain; masked tokens (only in a
+        // range's last tile) get weight 0
+        const int g0 = t * kTile;
+        const bool full = g0 + kTile <= count;
+        float mt = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sv[v] = s[v];
-        if (!full && g0 + acc_token(v, half) >= count) sv[v] = -INFINITY;
-        mt = fmaxf(mt, sv[v]);
+        for (int v = 0; v < 16; ++v) {
+          if (!full && g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
+          mt = fmaxf(mt, s[v]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+        if (m_base == -INFINITY) m_base = mt;  // first tile (every tile has a kept row)
+        m_seen = fmaxf(m_seen, mt);
+        redo |= mt > m_base + kMaxExp;
+        float psum = 0.f;
+        uint16_t* pw = pbuf[(t - t_begin) & 1];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 ph, pl;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], scale_log2, -m_base));
+            const float p1 =
+                __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], scale_log2, -m_base));
+            psum += p0 + p1;
+            const uint32_t hi = pack_bf16x2(p0, p1);
+            ph[w] = hi;
+            pl[w] = pack_bf16x2(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
+          }
+          // tokens 16 ks + 8 half .. + 7 of head `head`: chunk 2 ks + half
+          *(u32x4*)(pw + p_offset(0, head, 2 * ks + half)) = ph;
+          *(u32x4*)(pw + p_offset(1, head, 2 * ks + half)) = pl;
+        }
+        l_run += psum + __shfl_xor(psum, 32);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-      if (m_base == -INFINITY) m_base = mt;  // first tile (every tile has a kept row)
-      m_seen = fmaxf(m_seen, mt);
-      redo |= mt > m_base + kMaxExp;
-      // P = P_hi + P_lo as bf16 pairs; tokens 0..15 (ks = 0) now, tokens
-      // 16..31 while the first half's products run
-      float psum = 0.f;
-      u32x4 ph[2], pl[2];
-      auto make_p = [&](int ks, int w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w], scale_log2, -m_base));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w + 1], scale_log2, -m_base));
-        psum += p0 + p1;
-        const uint32_t hi = pack_bf16x2(p0, p1);
-        ph[ks][w] = hi;
-        pl[ks][w] = pack_bf16x2(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
-      };
-#pragma unroll
-      for (int w = 0; w < 4; ++w) make_p(0, w);
 
-      // ---- O^T += V^T P^T (P as bf16 hi + lo).  V^T operands are read
-      // kDepthV value blocks ahead; the scheduling barriers keep the
-      // compiler from sinking the reads back next to their products.
-      constexpr int kDepthV = 3, kRingV = kDepthV + 2;
-      bf16x8 vr[kRingV];
+      if (t > t_begin) {
+        // ---- O^T += V^T P^T for tile t - 1: this wave's 128 value columns,
+        // all 128 heads.  Per token half: the P^T operands of the 4 head
+        // blocks (hi and lo) from LDS, then per value block one transposed
+        // V^T read serving 8 products.
+        const uint16_t* tile = tiles[(t - 1 - t_begin) % kBufs];
+        const uint16_t* pr = pbuf[(t - 1 - t_begin) & 1];
 #pragma unroll
-      for (int j = 0; j < kDepthV; ++j) vr[j] = load_vt32(tile, j % kDVB, j / kDVB, lane);
-      // Product i (i = ks * kDVB + d) adds its bf16-hi part, then the lo part
-      // of product i - 1, so consecutive MFMAs never share an accumulator.
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 bh[kHB], bl[kHB];
 #pragma unroll
-      for (int i = 0; i <= 2 * kDVB; ++i) {
-        if (i + kDepthV < 2 * kDVB) {
-          const int n = i + kDepthV;
-          vr[n % kRingV] = load_vt32(tile, n % kDVB, n / kDVB, lane);
+          for (int hb = 0; hb < kHB; ++hb) {
+            const int h = 32 * hb + (lane & 31);
+            bh[hb] = as_bf16x8(*(const u32x4*)(pr + p_offset(0, h, 2 * ks + half)));
+            bl[hb] = as_bf16x8(*(const u32x4*)(pr + p_offset(1, h, 2 * ks + half)));
+          }
+          bf16x8 va = load_vt32(tile, c_wave, ks, lane);
+#pragma unroll
+          for (int d = 0; d < kDVB; ++d) {
+            const bf16x8 vcur = va;
+            if (d + 1 < kDVB) va = load_vt32(tile, c_wave + 32 * (d + 1), ks, lane);
+#pragma unroll
+            for (int hb = 0; hb < kHB; ++hb) o[hb][d] = mfma32(vcur, bh[hb], o[hb][d]);
+#pragma unroll
+            for (int hb = 0; hb < kHB; ++hb) o[hb][d] = mfma32(vcur, bl[hb], o[hb][d]);
+          }
         }
-        if (i < 2 * kDVB) {
-          const int ks = i / kDVB, d = i % kDVB;
-          o[d] = mfma32(vr[i % kRingV], as_bf16x8(ph[ks]), o[d]);
-        }
-        if (i > 0) {
-          const int ks = (i - 1) / kDVB, d = (i - 1) % kDVB;
-          o[d] = mfma32(vr[(i - 1) % kRingV], as_bf16x8(pl[ks]), o[d]);
-        }
-        if (i >= 1 && i <= 4) make_p(1, i - 1);
-        __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += psum + __shfl_xor(psum, 32);
     }
   }
-  const float m_run = m_base;
 
-  // ---- epilogue: lane holds head `head`, value columns
-  // 32 d + 8 (v / 4) + 4 half + v % 4
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse_val = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+  // ---- epilogue.  Head statistics go through LDS from their owners to the
+  // waves holding the value columns.
+  const float lse_val = l_run > 0.f ? (m_base + __log2f(l_run)) * kLn2 : -INFINITY;
+  if (half == 0) {
+    head_l[head] = l_run;
+    head_lse[head] = lse_val;
+  }
+  __syncthreads();
+  // lane holds head 32 hb + lane % 32 and value columns
+  // c_wave + 32 d + 8 (v / 4) + 4 half + v % 4
   if (n_splits == 1) {
-    uint16_t* orow = out + ((int64_t)qi * kHeads + head) * kDv + 4 * half;
 #pragma unroll
-    for (int d = 0; d < kDVB; ++d)
+    for (int hb = 0; hb < kHB; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      const float lh = head_l[h];
+      const float inv_l = lh > 0.f ? 1.f / lh : 0.f;
+      uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kDv + c_wave + 4 * half;
 #pragma unroll
-      for (int bq = 0; bq < 4; ++bq) {
-        const uint32_t lo = pack_bf16x2(o[d][4 * bq] * inv_l, o[d][4 * bq + 1] * inv_l);
-        const uint32_t hi = pack_bf16x2(o[d][4 * bq + 2] * inv_l, o[d][4 * bq + 3] * inv_l);
-        *(uint2*)(orow + 32 * d + 8 * bq) = make_uint2(lo, hi);
-      }
+      for (int d = 0; d < kDVB; ++d)
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq) {
+          const uint32_t lo = pack_bf16x2(o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l);
+          const uint32_t hi =
+              pack_bf16x2(o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l);
+          *(uint2*)(orow + 32 * d + 8 * bq) = make_uint2(lo, hi);
+        }
+    }
     if (lse && half == 0) lse[(int64_t)qi * kHeads + head] = lse_val;
   } else {
-    const int64_t pidx = ((int64_t)qi * n_splits + split) * kHeads + head;
-    float* prow = part_o + pidx * kDv + 4 * half;
 #pragma unroll
-    for (int d = 0; d < kDVB; ++d)
+    for (int hb = 0; hb < kHB; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      const float lh = head_l[h];
+      const float inv_l = lh > 0.f ? 1.f / lh : 0.f;
+      const int64_t pidx = ((int64_t)qi * n_splits + split) * kHeads + h;
+      float* prow = part_o + pidx * kDv + c_wave + 4 * half;
 #pragma unroll
-      for (int bq = 0; bq < 4; ++bq)
-        *(f32x4*)(prow + 32 * d + 8 * bq) =
-            f32x4{o[d][4 * bq] * inv_l, o[d][4 * bq + 1] * inv_l, o[d][4 * bq + 2] * inv_l,
-                  o[d][4 * bq + 3] * inv_l};
-    if (half == 0) part_lse[pidx] = lse_val;
+      for (int d = 0; d < kDVB; ++d)
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq)
+          *(f32x4*)(prow + 32 * d + 8 * bq) =
+              f32x4{o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l,
+                    o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l};
+    }
+    if (half == 0) part_lse[((int64_t)qi * n_splits + split) * kHeads + head] = lse_val;
   }
 }
 
