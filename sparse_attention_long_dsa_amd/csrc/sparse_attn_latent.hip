@@ -111,6 +111,18 @@ __device__ __forceinline__ void mfma_result_fence(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
+// op(x, x of lane l ^ 32) in every lane l, by the gfx950 swap of the two
+// 32-lane halves of a register pair: after the swap the first register holds
+// (x[0..31], x[0..31]) and the second (x[32..63], x[32..63]).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Token held in accumulator slot v by a lane of half h (= lane / 32):
 // 8 h + (v % 8) for v < 8, 16 + 8 h + (v % 8) for v >= 8.  Accumulator row
 // m of the 32x32 result holds token perm(m), so the A operand reads row
@@ -300,13 +312,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
         // range's last tile) get weight 0
         const int g0 = t * kTile;
         const bool full = g0 + kTile <= count;
+        if (!full) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
+        }
         float mt = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (!full && g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
-          mt = fmaxf(mt, s[v]);
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[v]);
+        mt = halves_max(mt) * scale_log2;
         if (m_base == -INFINITY) m_base = mt;  // first tile (every tile has a kept row)
         m_seen = fmaxf(m_seen, mt);
         redo |= mt > m_base + kMaxExp;
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           *(u32x4*)(pw + p_offset(0, head, 2 * ks + half)) = ph;
           *(u32x4*)(pw + p_offset(1, head, 2 * ks + half)) = pl;
         }
-        l_run += psum + __shfl_xor(psum, 32);
+        l_run += halves_sum(psum);
       }
 
       if (t > t_begin) {
