@@ -38,6 +38,13 @@
  *                 with a separate V pool;
  *       1 <= K <= 2048; any lengths; block_size a multiple of 16 for
  *       dsa_index_score, any block_size >= 1 for the other calls.
+ *   - Precision of attention: q.K in bf16 with fp32 accumulation.  In the
+ *     (128, 576, 512) family the P.V product runs in fp16 with fp32
+ *     accumulation: the weights carry 11 significant bits and the values are
+ *     converted from bf16, exactly for magnitudes in [2^-17, 65504], so value
+ *     entries must stay within the fp16 range (|v| <= 65504).  The (8, 64, 64)
+ *     family carries each weight as a bf16 pair (16 bits) and has no range
+ *     limit beyond bf16's.
  */
 #ifndef DSA_H
 #define DSA_H

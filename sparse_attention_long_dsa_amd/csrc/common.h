@@ -35,10 +35,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// Two floats -> packed fp16 pair, round to nearest even.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 pair, round to nearest even: one gfx950
+// v_cvt_pk_f16_f32.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+// Eight bf16 (packed in pairs) -> eight fp16.  Exact for magnitudes in
+// [2^-17, 65504]; smaller ones keep an absolute error below 2^-25.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(bf16_lo(v[i]), bf16_hi(v[i]));
+  return as_f16x8(r);
 }
 __device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

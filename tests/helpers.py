@@ -43,11 +43,21 @@ def gpu_prefill(dc, pos0=0, T=None, seq=0):
     return step
 
 
-def assert_attention(got_out, got_lse, ref_out, ref_lse, what=""):
+def assert_attention(got_out, got_lse, ref_out, ref_lse, what="", rel=False):
+    """rel=True replaces the flat max-abs bar by a per-element one,
+    2^-8 |ref| + 2e-3: rounding the output to bf16 alone costs up to 2^-8
+    relative (8 significant bits), which passes 1e-2 once |ref| >= 2.56 -- a
+    peaked softmax puts single value entries (up to ~5 for N(0,1) data)
+    straight into the output.  2e-3 covers the arithmetic (fp16 weights,
+    fp32 sums)."""
     g = got_out.float().cpu().numpy() if torch.is_tensor(got_out) else got_out
     err = np.abs(g - ref_out)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
-    assert err.max() <= ATOL_MAX, f"{what}: max|err| {err.max():.3e}"
+    if rel:
+        excess = err - (np.abs(ref_out) * 2.0**-8 + 2e-3)
+        assert excess.max() <= 0, f"{what}: err above 2^-8|ref| + 2e-3 by {excess.max():.3e}"
+    else:
+        assert err.max() <= ATOL_MAX, f"{what}: max|err| {err.max():.3e}"
     assert err.mean() <= ATOL_MEAN, f"{what}: mean|err| {err.mean():.3e}"
     if got_lse is not None:
         gl = got_lse.cpu().numpy() if torch.is_tensor(got_lse) else got_lse
