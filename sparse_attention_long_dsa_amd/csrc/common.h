@@ -66,22 +66,50 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Direct global -> LDS load of 16 bytes a lane (lane l fills LDS bytes
+// lds + 16 l .. + 15), written out so that the compiler does not track it:
+// it would otherwise wait for every such load in flight before each LDS read,
+// which serialises the loads of the next tile with the current tile's
+// products.  Completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that hands a tile to its readers.  M0 is saved and restored.
+__device__ __forceinline__ void global_to_lds16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
 // Physical pool row of logical position `pos` of the sequence whose block
 // table row is `bt_row`.
 __device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt_row, int bs, int pos) {
   return (int64_t)bt_row[pos / bs] * bs + pos % bs;
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
+// The gfx950 row swaps: after permlane16_swap(x, x) the first register holds
+// rows (x0, x0, x2, x2) and the second (x1, x1, x3, x3) (a row is 16 lanes);
+// after permlane32_swap(x, x) they hold halves (x_lo, x_lo) and (x_hi, x_hi).
+// So op(first, second) is op(x, x of lane l ^ 16), resp. l ^ 32, in every
+// lane, with no LDS round trip.
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+__device__ __forceinline__ float wave_max_xor_16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// max(x, 0) as one integer max on the bit pattern (negative floats have
+// negative patterns), without the NaN canonicalisation fmaxf brings along.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Order-preserving map of fp32 onto uint32: larger float -> larger key.
 // -0.0 is folded onto +0.0 so the two compare equal.

@@ -17,7 +17,8 @@
 // MFMA operand registers (a lane loads 16 contiguous bytes of one key row);
 // the query stays in registers.  Prefill (item (3): compute bound): each
 // workgroup stages a tile of keys in LDS once and reuses it for a block of
-// queries, so keys are read from HBM once per query block.
+// queries; the query block keeps its queries in registers over a long run
+// of key tiles.
 #include <algorithm>
 
 #include "common.h"
@@ -105,7 +106,7 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += wr[ht][i] * fmaxf(acc[ht][i], 0.f);
+        for (int i = 0; i < 4; ++i) s += wr[ht][i] * relu(acc[ht][i]);
       s = wave_sum_xor_16_32(s);
       const int tok = base + 16 * u + col;
       if (grp == 0 && tok >= t0 && tok < t1) out[tok] = s;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
 // ---------------------------------------------------------------- prefill
 
 template <int H_IDX, int D_IDX, int QB, int KB>
-__global__ __launch_bounds__(kThreads) void index_score_prefill_kernel(
+__global__ __launch_bounds__(kThreads) void index_score_prefill_tile_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ bt_row,
     int bs, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int n_q, int pos0,
     float* __restrict__ scores, int64_t ld) {
@@ -274,9 +275,147 @@ __global__ __launch_bounds__(kThreads) void index_score_prefill_kernel(
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += wr[ht][i] * fmaxf(acc[ht][i], 0.f);
+        for (int i = 0; i < 4; ++i) s += wr[ht][i] * relu(acc[ht][i]);
       s = wave_sum_xor_16_32(s);
       if (grp == 0 && 16 * g + col < n) out[16 * g + col] = s;
+    }
+  }
+}
+
+// Wide indexer (H_IDX x 128 dims, H_IDX a multiple of 16): one workgroup
+// takes 16 consecutive queries and a chunk of up to kChunk key tiles of 128
+// positions.  Each of its 16 waves keeps one query in registers for the
+// whole chunk, so a query is read once per chunk rather than once per key
+// tile, and every key tile staged in LDS serves 16 queries; key tiles go
+// from HBM straight into LDS (direct loads, one tile ahead, no registers).
+// Four waves per SIMD hide the LDS latency and overlap one wave's
+// ReLU-weight-sum epilogue with another's products.  A tile row's sixteen 16-byte chunks are XOR-swizzled
+// by the row index, so the 16 lanes that read 16 rows at one chunk hit 16
+// different bank groups; the direct loads honour the same map.
+namespace pf {
+constexpr int kWaves = 16, kThreads = kWaves * kWave;
+constexpr int kQW = 1;                                // queries per wave
+constexpr int kQB = kWaves * kQW;                     // queries per workgroup
+constexpr int kKT = 128;                              // keys per tile
+constexpr int kChunk = 64;                            // tiles per workgroup at most (8192 keys)
+constexpr int kD = 128;
+constexpr int kRowChunks = kD / 8;                    // 16-byte chunks per key row
+constexpr int kTileBytes = kKT * kD * 2;              // 32 KB
+constexpr int kLoads = kTileBytes / (16 * kThreads);  // wave loads per wave per tile
+}  // namespace pf
+
+template <int H_IDX>
+__global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ bt_row,
+    int bs, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int n_q, int pos0,
+    float* __restrict__ scores, int64_t ld) {
+  using pf::kChunk, pf::kD, pf::kKT, pf::kLoads, pf::kQB, pf::kQW, pf::kRowChunks,
+      pf::kTileBytes;
+  constexpr int HT = H_IDX / 16, KS = kD / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
+  __shared__ int32_t prow[kChunk * kKT];
+
+  // the longest query blocks (latest positions) first, so that the short ones
+  // fill in behind them
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * kQB;
+  const int qend = min(q0 + kQB, n_q);
+  const int last_pos = pos0 + qend - 1;  // largest query position of the workgroup
+  const int k_begin = blockIdx.x * (kChunk * kKT);
+  if (k_begin > last_pos) return;
+  const int k_end = min(k_begin + kChunk * kKT, last_pos + 1);
+  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
+
+  // physical rows of the chunk's keys; slots past k_end repeat the first
+  // key (finite data, never stored)
+  for (int r = threadIdx.x; r < n_tiles * kKT; r += pf::kThreads) {
+    const int pos = k_begin + r;
+    prow[r] = (int32_t)paged_row(bt_row, bs, pos < k_end ? pos : k_begin);
+  }
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15, grp = lane >> 4;
+
+  // this wave's queries: q as the A operand (head 16 ht + col, dims
+  // 32 ks + 8 grp ..), the weights of the heads in this lane's result rows
+  bf16x8 qa[kQW][HT][KS];
+  float wr[kQW][HT][4];
+  int qpos[kQW];
+#pragma unroll
+  for (int qq = 0; qq < kQW; ++qq) {
+    const int qi = q0 + kQW * wave + qq;
+    const bool ok = qi < qend;
+    qpos[qq] = ok ? pos0 + qi : -1;
+    const int qr = ok ? qi : q0;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[qq][ht][ks] = as_bf16x8(
+            *(const u32x4*)(q_idx + ((int64_t)qr * H_IDX + 16 * ht + col) * kD + 32 * ks + 8 * grp));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[qq][ht][i] = w[(int64_t)qr * H_IDX + 16 * ht + 4 * grp + i];
+    }
+  }
+  __syncthreads();  // prow
+
+  // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
+  // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ktile;
+  const uint64_t row_bytes = (uint64_t)k_stride * 2;
+  auto load_tile = [&](int j, int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int blk = kLoads * wave + i;
+      const int slot = kWave * blk + lane;
+      const int r = slot / kRowChunks;
+      const int c = (slot % kRowChunks) ^ (r % kRowChunks);
+      const char* src = (const char*)k_idx + (uint64_t)(uint32_t)prow[j * kKT + r] * row_bytes + 16 * c;
+      global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * blk));
+    }
+  };
+  load_tile(0, 0);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
+    __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
+    if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
+    const uint16_t* kt = ktile[j & 1];
+    const int k0 = k_begin + j * kKT;
+    int n[kQW], n_max = 0;  // keys of this tile each query sees (wave-uniform)
+#pragma unroll
+    for (int qq = 0; qq < kQW; ++qq) {
+      n[qq] = min(kKT, max(0, qpos[qq] + 1 - k0));
+      n_max = max(n_max, n[qq]);
+    }
+    for (int g = 0; 16 * g < n_max; ++g) {
+      f32x4 acc[kQW][HT];
+#pragma unroll
+      for (int qq = 0; qq < kQW; ++qq)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
+        const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
+#pragma unroll
+        for (int qq = 0; qq < kQW; ++qq)
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = mfma16x16x32(qa[qq][ht][ks], kb, acc[qq][ht]);
+      }
+#pragma unroll
+      for (int qq = 0; qq < kQW; ++qq) {
+        if (16 * g >= n[qq]) continue;
+        float sc = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc += wr[qq][ht][i] * relu(acc[qq][ht][i]);
+        sc = wave_sum_xor_16_32(sc);
+        if (grp == 0 && r < n[qq])
+          scores[(int64_t)(qpos[qq] - pos0) * ld + k0 + r] = sc;
+      }
     }
   }
 }
@@ -317,11 +456,23 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
                          c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
                          c->block_size, c->seq_lens, q_idx, w, scores, ld, chunk);
     }
+  } else if constexpr (D_IDX == pf::kD && H_IDX % 16 == 0) {
+    const int64_t n_keys = (int64_t)pos0 + n_q;
+    const int64_t nchunks = (n_keys + pf::kChunk * pf::kKT - 1) / (pf::kChunk * pf::kKT);
+    const int64_t nqb = ((int64_t)n_q + pf::kQB - 1) / pf::kQB;
+    if (nqb > 65535) return DSA_ERR_SHAPE;
+    // a workgroup covers up to 8192 keys of 16 queries: a whole row for
+    // prefixes up to 8192, so the per-workgroup start (block-table lookups,
+    // q loads, first tile) is paid once per query block
+    hipLaunchKernelGGL((index_score_prefill_kernel<H_IDX>), dim3((unsigned)nchunks, (unsigned)nqb),
+                       dim3(pf::kThreads), 0, stream, c->k_idx, c->k_idx_row_stride,
+                       c->block_table + (int64_t)seq * c->max_blocks_per_seq, c->block_size,
+                       q_idx, w, n_q, pos0, scores, ld);
   } else {
     constexpr int QB = 64, KB = 128;
     const int64_t nkt = ((int64_t)pos0 + n_q + KB - 1) / KB;
     const int64_t nqb = ((int64_t)n_q + QB - 1) / QB;
-    hipLaunchKernelGGL((index_score_prefill_kernel<H_IDX, D_IDX, QB, KB>),
+    hipLaunchKernelGGL((index_score_prefill_tile_kernel<H_IDX, D_IDX, QB, KB>),
                        dim3((unsigned)nkt, (unsigned)nqb), dim3(kThreads), 0, stream, c->k_idx,
                        c->k_idx_row_stride,
                        c->block_table + (int64_t)seq * c->max_blocks_per_seq, c->block_size,

@@ -62,23 +62,6 @@ constexpr int kMaxTiles = 2048 / kTile;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Direct global -> LDS load of 16 bytes a lane (lane l fills LDS bytes
-// lds + 16 l .. + 15), written out so that the compiler does not track it:
-// it would otherwise wait for every such load in flight before each LDS read,
-// which serialises the loads of the next tile with the current tile's
-// products.  Completion is awaited explicitly (s_waitcnt vmcnt) before the
-// barrier that hands a tile to its readers.  M0 is saved and restored.
-__device__ __forceinline__ void global_to_lds16(const void* src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
-}
 // The same load with a wave-uniform 64-bit base in SGPRs and a per-lane
 // 32-bit byte offset (no vector address arithmetic).
 __device__ __forceinline__ void global_to_lds16_s(const void* base, uint32_t off, uint32_t lds) {
