@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_decode_traffic.json")
-INDEX_SRC = os.path.join(ROOT, "sparse_attention_long_dsa_amd", "csrc", "index_score.hip")
+# the decode index kernel's sources (its file and the shared device helpers)
+INDEX_SRC = [os.path.join(ROOT, "sparse_attention_long_dsa_amd", "csrc", f)
+             for f in ("index_score.hip", "common.h")]
 
 
 def decode_bytes(wl):
@@ -58,8 +60,11 @@ def prefill_flops(wl):
     return 2 * wl.d_idx * wl.H_idx * pairs, 2 * wl.H * (wl.d_qk + wl.d_v) * kept
 
 
-def sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
 
 
 def traffic_for(kernel_launches=1):
