@@ -31,6 +31,10 @@
  *     contents (block table entries, lengths, indices) are trusted: they are
  *     not read on the host.  A launch failure returns DSA_ERR_HIP.
  *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Alignment: kv, v, k_idx, q, q_idx, out and the attention workspace
+ *     must start 16-byte aligned and row strides must be multiples of 8
+ *     elements (every HIP and torch allocation is aligned); otherwise
+ *     DSA_ERR_UNSUPPORTED.
  *   - Shapes supported by the kernels (others return DSA_ERR_UNSUPPORTED):
  *       indexer   (H_idx, d_idx) = (64, 128) or (4, 32);
  *       attention (H, d_qk, d_v) = (128, 576, 512) with V the first 512

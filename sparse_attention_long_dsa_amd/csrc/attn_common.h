@@ -40,21 +40,23 @@ inline SplitPlan plan_splits_latent(int B, int K) {
 namespace {
 
 // Log-sum-exp merge of the split-K partial results: one workgroup per
-// (query, head); each thread owns value dims.
+// (query, head); thread t owns value dims 4 t .. 4 t + 3 (16-byte loads,
+// 8-byte stores), looping when D_V > 4 * 128.
 template <int D_V>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            int n_splits, int H,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse) {
+  static_assert(D_V % 4 == 0, "value width must be a multiple of 4");
+  constexpr int kPer = (D_V / 4 + 127) / 128;
   const int qh = blockIdx.x;  // qi * H + head
   const int qi = qh / H, head = qh % H;
   float m = -INFINITY;
   for (int s = 0; s < n_splits; ++s)
     m = fmaxf(m, part_lse[((int64_t)qi * n_splits + s) * H + head]);
   float wsum = 0.f;
-  float acc[D_V / 128 > 0 ? D_V / 128 : 1] = {};
-  constexpr int kPer = D_V / 128 > 0 ? D_V / 128 : 1;
+  f32x4 acc[kPer] = {};
   for (int s = 0; s < n_splits; ++s) {
     const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
     const float l = part_lse[p];
@@ -62,15 +64,18 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     wsum += wgt;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int d = threadIdx.x + 128 * e;
-      if (d < D_V) acc[e] += wgt * part_o[p * D_V + d];
+      const int d = 4 * (threadIdx.x + 128 * e);
+      if (d < D_V) acc[e] += wgt * *(const f32x4*)(part_o + p * D_V + d);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int d = threadIdx.x + 128 * e;
-    if (d < D_V) out[(int64_t)qh * D_V + d] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+    const int d = 4 * (threadIdx.x + 128 * e);
+    if (d < D_V)
+      *(uint2*)(out + (int64_t)qh * D_V + d) =
+          make_uint2(pack_bf16x2(acc[e][0] * inv, acc[e][1] * inv),
+                     pack_bf16x2(acc[e][2] * inv, acc[e][3] * inv));
   }
   if (lse && threadIdx.x == 0) lse[qh] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }

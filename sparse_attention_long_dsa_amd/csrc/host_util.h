@@ -27,6 +27,10 @@ inline dsa_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
+// The kernels move 16-byte vectors: device buffers must start 16-byte
+// aligned (every allocation of the HIP runtime and of torch is).
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 // Checks of the paged-cache description common to every call.
 inline dsa_status_t check_cache_common(const dsa_paged_cache_t* c) {
   if (!c || !c->block_table) return DSA_ERR_NULL;

@@ -507,6 +507,7 @@ extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phas
   const bool small = H_idx == 4 && cache->d_idx == 32;
   if (!big && !small) return DSA_ERR_UNSUPPORTED;
   if (cache->k_idx_row_stride % 8 != 0) return DSA_ERR_UNSUPPORTED;  // 16-byte row alignment
+  if (!aligned16(cache->k_idx) || !aligned16(q_idx)) return DSA_ERR_UNSUPPORTED;
   if (cache->block_size % 16 != 0) return DSA_ERR_UNSUPPORTED;        // 16-position groups
   st = check_device();
   if (st != DSA_OK) return st;

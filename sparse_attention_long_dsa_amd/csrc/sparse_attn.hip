@@ -347,6 +347,8 @@ dsa_status_t check_attn_args(const dsa_paged_cache_t* c, const uint16_t* q, cons
   *fam = family_of(c, H);
   if (*fam == kNone) return DSA_ERR_UNSUPPORTED;
   if (c->kv_row_stride % 8 != 0 || (c->v && c->v_row_stride % 8 != 0)) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(c->kv) || (c->v && !aligned16(c->v)) || !aligned16(q) || !aligned16(out))
+    return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -399,6 +401,7 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
   if (B != cache->n_seq) return DSA_ERR_SHAPE;
   const size_t need = dsa_sparse_attn_decode_workspace_size(B, H, K, cache->d_v);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return DSA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != DSA_OK) return st;
   const SplitPlan plan = decode_plan(B, H, K, cache->d_v);

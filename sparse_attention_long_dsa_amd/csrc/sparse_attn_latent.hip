@@ -244,9 +244,48 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     return as_bf16x8(*(const u32x4*)(tile + off));
   };
 
-  constexpr float kMaxExp = 15.f;  // weights stay below 2^15 (fp16 range)
   f32x16 o[kHB][kDVB];
   float m_base = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+
+  // weights of tokens 16 ks + 8 half .. + 7 of head `head` (fp16, packed)
+  auto weights_half = [&](const f32x16& sv, int ks, float& psum) {
+    u32x4 ph;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w], scale_log2, -m_base));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w + 1], scale_log2, -m_base));
+      psum += p0 + p1;
+      ph[w] = pack_f16x2(p0, p1);
+    }
+    return ph;
+  };
+  // token half ks of head `head` is chunk 2 ks + half of its P row
+  auto store_p = [&](uint16_t* pw, const u32x4& ph0, const u32x4& ph1) {
+    *(u32x4*)(pw + p_offset(head, half)) = ph0;
+    *(u32x4*)(pw + p_offset(head, 2 + half)) = ph1;
+  };
+  // O^T += V^T P^T for token half ks of a tile: this wave's 128 value
+  // columns, all 128 heads, fp16 operands: the P^T operands of the 4 head
+  // blocks from LDS, then per value block one transposed V^T read, converted
+  // to fp16, serving 4 products.
+  auto pv_half = [&](const uint16_t* tile, const uint16_t* pr, int ks) {
+    f16x8 bp[kHB];
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      bp[hb] = as_f16x8(*(const u32x4*)(pr + p_offset(h, 2 * ks + half)));
+    }
+    u32x4 va = load_vt32(tile, c_wave, ks, lane);
+#pragma unroll
+    for (int d = 0; d < kDVB; ++d) {
+      const f16x8 vcur = bf16x8_to_f16x8(va);
+      if (d + 1 < kDVB) va = load_vt32(tile, c_wave + 32 * (d + 1), ks, lane);
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) o[hb][d] = mfma32_f16(vcur, bp[hb], o[hb][d]);
+    }
+  };
+
+  constexpr float kMaxExp = 15.f;  // weights stay below 2^15 (fp16 range)
   bool redo = false;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
@@ -274,11 +313,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       const bool next = t + 1 < t_end;
       if (next) load_begin(t + 1, (t + 1 - t_begin) % kBufs);
 
+      f32x16 s;  // S^T of tile t: head `head`, tokens acc_token(v, half)
       if (have_s) {
         const uint16_t* tile = tiles[(t - t_begin) % kBufs];
         // ---- S^T = K Q^T; the A operands are read kDepthS k-steps ahead
         constexpr int kDepthS = 2, kRingS = kDepthS + 2;
-        f32x16 s;
         bf16x8 ar[kRingS];
 #pragma unroll
         for (int jj = 0; jj < kDepthS; ++jj) ar[jj] = a_operand(tile, jj);
@@ -310,49 +349,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
         if (m_base == -INFINITY) m_base = mt;  // first tile (every tile has a kept row)
         m_seen = fmaxf(m_seen, mt);
         redo |= mt > m_base + kMaxExp;
-        float psum = 0.f;
-        uint16_t* pw = pbuf[(t - t_begin) & 1];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4 ph;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], scale_log2, -m_base));
-            const float p1 =
-                __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], scale_log2, -m_base));
-            psum += p0 + p1;
-            ph[w] = pack_f16x2(p0, p1);
-          }
-          // tokens 16 ks + 8 half .. + 7 of head `head`: chunk 2 ks + half
-          *(u32x4*)(pw + p_offset(head, 2 * ks + half)) = ph;
-        }
-        l_run += halves_sum(psum);
       }
 
+      // ---- the weights of tile t and O += V P of tile t - 1.  In the steady
+      // state both go into one block, so that the scheduler can hide the
+      // softmax arithmetic under the products; the weights are stored after
+      // the last read of the other P buffer.
+      const uint16_t* v_tile = tiles[(t + kBufs - 1 - t_begin) % kBufs];
+      const uint16_t* pr = pbuf[(t - 1 - t_begin) & 1];
+      uint16_t* pw = pbuf[(t - t_begin) & 1];
+      float psum = 0.f;
+      if (have_s) {
+        const u32x4 ph0 = weights_half(s, 0, psum);
+        const u32x4 ph1 = weights_half(s, 1, psum);
+        store_p(pw, ph0, ph1);
+        l_run += halves_sum(psum);
+      }
       if (t > t_begin) {
-        // ---- O^T += V^T P^T for tile t - 1: this wave's 128 value columns,
-        // all 128 heads, fp16 operands.  Per token half: the P^T operands of
-        // the 4 head blocks from LDS, then per value block one transposed
-        // V^T read, converted to fp16, serving 4 products.
-        const uint16_t* tile = tiles[(t - 1 - t_begin) % kBufs];
-        const uint16_t* pr = pbuf[(t - 1 - t_begin) & 1];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f16x8 bp[kHB];
-#pragma unroll
-          for (int hb = 0; hb < kHB; ++hb) {
-            const int h = 32 * hb + (lane & 31);
-            bp[hb] = as_f16x8(*(const u32x4*)(pr + p_offset(h, 2 * ks + half)));
-          }
-          u32x4 va = load_vt32(tile, c_wave, ks, lane);
-#pragma unroll
-          for (int d = 0; d < kDVB; ++d) {
-            const f16x8 vcur = bf16x8_to_f16x8(va);
-            if (d + 1 < kDVB) va = load_vt32(tile, c_wave + 32 * (d + 1), ks, lane);
-#pragma unroll
-            for (int hb = 0; hb < kHB; ++hb) o[hb][d] = mfma32_f16(vcur, bp[hb], o[hb][d]);
-          }
-        }
+        pv_half(v_tile, pr, 0);
+        pv_half(v_tile, pr, 1);
       }
     }
   }

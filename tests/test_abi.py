@@ -75,6 +75,8 @@ def test_index_score_validation(L):
     assert score(L, cache(k_idx_row_stride=100)) == 2        # stride below width
     assert score(L, cache()) == 5                            # well formed: no gfx950 here
     assert score(L, cache(d_idx=32, k_idx_row_stride=32), H=4) == 5
+    assert score(L, cache(k_idx=FAKE + 8)) == 3              # 16-byte alignment
+    assert score(L, cache(), q=FAKE + 4) == 3
 
 
 def test_topk_validation(L):
@@ -115,3 +117,11 @@ def test_attention_validation(L):
     assert pre(ctypes.byref(c), FAKE, FAKE, 300, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 2
     assert pre(ctypes.byref(c), FAKE, FAKE, 100, 128, 2048, 5, 0, 0.1, FAKE, None, None) == 2
     assert pre(ctypes.byref(c), None, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 1
+    # 16-byte alignment of the vector-loaded buffers
+    for bad in (dict(kv=FAKE + 2),):
+        assert dec(ctypes.byref(cache(**bad)), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE,
+                   ws, None) == 3
+    assert dec(ctypes.byref(c), FAKE + 8, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 3
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE + 4, None, FAKE, ws, None) == 3
+    assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE + 4, ws, None) == 3
+    assert pre(ctypes.byref(c), FAKE + 2, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 3
