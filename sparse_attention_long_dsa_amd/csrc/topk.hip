@@ -44,7 +44,7 @@ namespace dsa {
 namespace {
 
 constexpr int kShortMax = 16384;    // longest row of the one-workgroup path
-constexpr int kShortThreads = 256;
+constexpr int kShortThreads = 512;
 constexpr int kChunk = 4096;        // positions per workgroup of the chunk step
 constexpr int kChunkThreads = 256;
 constexpr int kSampleThreads = 1024;  // sample step: one workgroup per row

@@ -128,6 +128,18 @@ def test_latent_prefill_chunk():
                   pos0=300, T=400)
 
 
+def test_latent_prefill_chunk_past_8192_keys():
+    # the prefill indexer covers at most 8192 keys per workgroup: positions
+    # 9000..9039 see two key chunks (the second one partial)
+    check_prefill(dsa_synth.latent("prefill_long", "prefill", [9040], seed=35, topk=2048),
+                  pos0=9000, T=40)
+
+
+def test_latent_prefill_single_query():
+    check_prefill(dsa_synth.latent("prefill_one", "prefill", [300], seed=36, topk=256),
+                  pos0=299, T=1)
+
+
 def test_latent_prefill_peaked_softmax():
     wl = dsa_synth.latent("prefill_peaked", "prefill", [600], seed=34, topk=256)
     check_prefill(dataclasses.replace(wl, sm_scale=1.0), rel=True)
