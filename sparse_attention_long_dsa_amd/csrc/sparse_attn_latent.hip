@@ -265,16 +265,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     *(u32x4*)(pw + p_offset(head, 2 + half)) = ph1;
   };
   // O^T += V^T P^T for token half ks of a tile: this wave's 128 value
-  // columns, all 128 heads, fp16 operands: the P^T operands of the 4 head
-  // blocks from LDS, then per value block one transposed V^T read, converted
-  // to fp16, serving 4 products.
-  auto pv_half = [&](const uint16_t* tile, const uint16_t* pr, int ks) {
-    f16x8 bp[kHB];
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) {
-      const int h = 32 * hb + (lane & 31);
-      bp[hb] = as_f16x8(*(const u32x4*)(pr + p_offset(h, 2 * ks + half)));
-    }
+  // columns, all 128 heads, fp16 operands: bp holds the P^T operands of the
+  // 4 head blocks; per value block one transposed V^T read, converted to
+  // fp16, serves 4 products.
+  auto pv_ops = [&](const uint16_t* tile, const f16x8* bp, int ks) {
     u32x4 va = load_vt32(tile, c_wave, ks, lane);
 #pragma unroll
     for (int d = 0; d < kDVB; ++d) {
@@ -304,9 +298,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       for (int i = 0; i < kWaveBlocks; ++i) load_block(i);
     }
 
-    // iteration t: S and softmax of tile t (t < t_end), then O += V P of
-    // tile t - 1 (t > t_begin)
-    for (int t = t_begin; t <= t_end; ++t) {
+    // The products of "tile t_begin - 1" read a zeroed V region and zeroed
+    // weights (they add exactly 0), and the last iteration's S and weights
+    // are computed and dropped, so that every iteration runs the same code
+    // and the weights of tile t share one block with the products of tile
+    // t - 1.
+    {
+      uint32_t* zv = (uint32_t*)tiles[kBufs - 1];
+      for (int i = threadIdx.x; i < kLatRegion / 4; i += kThreads) zv[i] = 0u;
+      uint32_t* zp = (uint32_t*)pbuf[1];
+      for (int i = threadIdx.x; i < kPElems / 2; i += kThreads) zp[i] = 0u;
+    }
+    for (int t = t_begin; t <= t_end && t_begin < t_end; ++t) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t has landed (this wave's part)
       __syncthreads();  // ... all of it; P(t - 1) is written; tile t - 2 and P(t - 2) are free
       const bool have_s = t < t_end;
@@ -314,9 +317,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       if (next) load_begin(t + 1, (t + 1 - t_begin) % kBufs);
 
       f32x16 s;  // S^T of tile t: head `head`, tokens acc_token(v, half)
-      if (have_s) {
+      {
         const uint16_t* tile = tiles[(t - t_begin) % kBufs];
-        // ---- S^T = K Q^T; the A operands are read kDepthS k-steps ahead
         constexpr int kDepthS = 2, kRingS = kDepthS + 2;
         bf16x8 ar[kRingS];
 #pragma unroll
@@ -332,9 +334,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           if (next && ks < kWaveBlocks) load_block(ks);
         }
         mfma_result_fence(s);
-
-        // ---- softmax weights, log2 domain; masked tokens (only in a
-        // range's last tile) get weight 0
         const int g0 = t * kTile;
         const bool full = g0 + kTile <= count;
         if (!full) {
@@ -342,32 +341,35 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           for (int v = 0; v < 16; ++v)
             if (g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
         }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[v]);
-        mt = halves_max(mt) * scale_log2;
-        if (m_base == -INFINITY) m_base = mt;  // first tile (every tile has a kept row)
-        m_seen = fmaxf(m_seen, mt);
-        redo |= mt > m_base + kMaxExp;
       }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[v]);
+      mt = halves_max(mt) * scale_log2;
+      if (have_s && m_base == -INFINITY) m_base = mt;
+      if (have_s) m_seen = fmaxf(m_seen, mt);
+      redo |= have_s && mt > m_base + kMaxExp;
 
-      // ---- the weights of tile t and O += V P of tile t - 1.  In the steady
-      // state both go into one block, so that the scheduler can hide the
-      // softmax arithmetic under the products; the weights are stored after
-      // the last read of the other P buffer.
       const uint16_t* v_tile = tiles[(t + kBufs - 1 - t_begin) % kBufs];
-      const uint16_t* pr = pbuf[(t - 1 - t_begin) & 1];
+      const uint16_t* pr = pbuf[(t + 1 - t_begin) & 1];
       uint16_t* pw = pbuf[(t - t_begin) & 1];
-      float psum = 0.f;
-      if (have_s) {
+      {
+        // P(t - 1) operands are read, and this tile's weights stored, outside
+        // the products, so that no LDS write sits between them
+        f16x8 bp0[kHB], bp1[kHB];
+#pragma unroll
+        for (int hb = 0; hb < kHB; ++hb) {
+          bp0[hb] = as_f16x8(*(const u32x4*)(pr + p_offset(32 * hb + (lane & 31), half)));
+          bp1[hb] = as_f16x8(*(const u32x4*)(pr + p_offset(32 * hb + (lane & 31), 2 + half)));
+        }
+        float psum = 0.f;
         const u32x4 ph0 = weights_half(s, 0, psum);
         const u32x4 ph1 = weights_half(s, 1, psum);
+        const float tsum = halves_sum(psum);
+        if (have_s) l_run += tsum;
+        pv_ops(v_tile, bp0, 0);
+        pv_ops(v_tile, bp1, 1);
         store_p(pw, ph0, ph1);
-        l_run += halves_sum(psum);
-      }
-      if (t > t_begin) {
-        pv_half(v_tile, pr, 0);
-        pv_half(v_tile, pr, 1);
       }
     }
   }
