@@ -142,30 +142,34 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     float* __restrict__ scores, int64_t ld) {
   __shared__ int64_t cum[kFlatMaxSeq + 1];
-  __shared__ int64_t part[kThreads];
-  // exclusive prefix of the lengths: per-thread runs, then a serial pass over
-  // the per-thread totals by one lane
+  __shared__ int64_t wave_tot[kWaves];
+  // exclusive prefix of the lengths: per-thread runs, a scan across each
+  // wave's lanes, then the four wave totals
   const int per = (n_seq + kThreads - 1) / kThreads;
   const int s0 = threadIdx.x * per, s1 = min(s0 + per, n_seq);
   int64_t run = 0;
   for (int i = s0; i < s1; ++i) run += seq_lens[i];
-  part[threadIdx.x] = run;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t acc = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int64_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-    cum[n_seq] = acc;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int64_t incl = run;
+#pragma unroll
+  for (int d = 1; d < kWave; d *= 2) {
+    const int64_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
   }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
   __syncthreads();
-  run = part[threadIdx.x];
+  int64_t base = 0, total_all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    base += i < wv ? wave_tot[i] : 0;
+    total_all += wave_tot[i];
+  }
+  run = base + incl - run;  // exclusive prefix of this thread's run
   for (int i = s0; i < s1; ++i) {
     cum[i] = run;
     run += seq_lens[i];
   }
+  if (threadIdx.x == 0) cum[n_seq] = total_all;
   __syncthreads();
   const int64_t total = cum[n_seq];
   const int64_t lo = total * blockIdx.x / gridDim.x;
