@@ -299,10 +299,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     }
 
     // The products of "tile t_begin - 1" read a zeroed V region and zeroed
-    // weights (they add exactly 0), and the last iteration's S and weights
-    // are computed and dropped, so that every iteration runs the same code
-    // and the weights of tile t share one block with the products of tile
-    // t - 1.
+    // weights (they add exactly 0), and the last iteration's weights come
+    // from S = -inf and are dropped, so that the weights of tile t and the
+    // products of tile t - 1 run as one block in every iteration.
     {
       uint32_t* zv = (uint32_t*)tiles[kBufs - 1];
       for (int i = threadIdx.x; i < kLatRegion / 4; i += kThreads) zv[i] = 0u;
@@ -317,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       if (next) load_begin(t + 1, (t + 1 - t_begin) % kBufs);
 
       f32x16 s;  // S^T of tile t: head `head`, tokens acc_token(v, half)
-      {
+      if (have_s) {
         const uint16_t* tile = tiles[(t - t_begin) % kBufs];
         constexpr int kDepthS = 2, kRingS = kDepthS + 2;
         bf16x8 ar[kRingS];
@@ -341,6 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           for (int v = 0; v < 16; ++v)
             if (g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
         }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = -INFINITY;  // past the last tile: weights 0
       }
       float mt = -INFINITY;
 #pragma unroll
