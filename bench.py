@@ -140,9 +140,28 @@ def time_prefill(wl, steps, warmup, log):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     parts = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(3)]
-    del dc, cache, step
+    # the cache write of the whole sequence: its own rows written back from a
+    # contiguous copy (gathered untimed), so the pools end up unchanged
+    pos = torch.arange(T, dtype=torch.int32, device=dc.kv.device)
+    seq = torch.zeros_like(pos)
+    bt = dc.block_table[0].long()
+    rows = bt[pos.long() // wl.block_size] * wl.block_size + pos.long() % wl.block_size
+    kv_rows = dc.kv.reshape(-1, wl.d_qk)[rows].contiguous()
+    kidx_rows = dc.k_idx.reshape(-1, wl.d_idx)[rows].contiguous()
+    dsa.cache_write(cache, seq, pos, kv_rows, kidx_rows)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    a.record(stream)
+    for _ in range(reps):
+        dsa.cache_write(cache, seq, pos, kv_rows, kidx_rows)
+    b.record(stream)
+    torch.cuda.synchronize()
+    cw_ms = a.elapsed_time(b) / reps
+    cw_bytes = 2 * T * 2 * (wl.d_qk + wl.d_idx) + 2 * T * 4 + T * 4
+    del dc, cache, step, kv_rows, kidx_rows
     torch.cuda.empty_cache()
-    return elapsed * 1e3 / steps, parts
+    return elapsed * 1e3 / steps, parts, (cw_ms, cw_bytes)
 
 
 def cpu_baseline(wl, budget_s, log):
@@ -294,7 +313,7 @@ def main():
     }
     if not args.no_prefill:
         pw = dsa_synth.workload(3)
-        pms, parts = time_prefill(pw, max(2, args.steps // 4), 2, log)
+        pms, parts, (cw_ms, cw_bytes) = time_prefill(pw, max(2, args.steps // 4), 2, log)
         fi, fa = prefill_flops(pw)
         res["prefill"] = {
             "workload": pw.name, "tokens_per_s": round(pw.seq_lens[0] / (pms * 1e-3), 1),
@@ -304,6 +323,11 @@ def main():
             "attn_mfma_util": round(fa / (parts[2] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TF, 4),
             "index_mfma_util": round(fi / (parts[0] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TF, 4),
             "flops": fi + fa}
+        res["cache_write"] = {
+            "workload": f"{pw.name}: {pw.seq_lens[0]} tokens' latent and indexer rows",
+            "ms": round(cw_ms, 4), "bytes": cw_bytes,
+            "gbs": round(cw_bytes / (cw_ms * 1e-3) / 1e9, 1),
+            "frac": round(cw_bytes / (cw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, log)
     print(json.dumps(res), flush=True)

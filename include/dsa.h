@@ -161,6 +161,25 @@ dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t *cache, const uint1
                                      int32_t seq, int32_t pos0, float sm_scale, uint16_t *out,
                                      float *lse, hipStream_t stream);
 
+/* Cache write (page 1, section 3 item (2), the paged layout; page
+ * "Day-0 Adaptation of Ultra-Large-Scale MoE Models on Heterogeneous AI
+ * Accelerators", section 4: what a prefill writes is what a decode reads).
+ * Token i of sequence seq[i] at logical position pos[i] is stored in the
+ * physical row block_table[seq[i] * max_blocks_per_seq + pos[i] / block_size]
+ * * block_size + pos[i] % block_size of each pool: kv_new row i (d_qk
+ * columns) into kv, v_new row i (d_v columns) into v, k_idx_new row i (d_idx
+ * columns) into k_idx.  The pools are written in place through the cache's
+ * pointers.  kv_new: bf16 [n, d_qk]; v_new: bf16 [n, d_v], NULL exactly when
+ * cache->v is NULL (the latent family, whose V is part of the kv row);
+ * k_idx_new: bf16 [n, d_idx]; seq, pos: int32 [n].  A token whose sequence,
+ * position or physical block lies outside the cache description is skipped.
+ * Two tokens must not map to the same row (their order is then undefined).
+ * seq_lens is neither read nor updated.  n == 0 is a no-op. */
+dsa_status_t dsa_cache_write(const dsa_paged_cache_t *cache, const int32_t *seq,
+                             const int32_t *pos, int32_t n, const uint16_t *kv_new,
+                             const uint16_t *v_new, const uint16_t *k_idx_new,
+                             hipStream_t stream);
+
 /* Static text for a status code. */
 const char *dsa_status_string(dsa_status_t status);
 

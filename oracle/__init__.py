@@ -130,6 +130,31 @@ def sparse_attn(k_pool, v_pool, block_table, block_size, q, q_seq, idx, sm_scale
     return out, lse
 
 
+def cache_write(pool, block_table, block_size, seq, pos, new):
+    """Paged cache write, in place: token i of sequence seq[i] at logical
+    position pos[i] goes to physical row block_table[seq[i], pos[i] //
+    block_size] * block_size + pos[i] % block_size of `pool` (viewed as
+    [rows, width]); new[i] fills the first new.shape[1] columns of that row.
+    Tokens whose sequence, position or block lies outside the table or the
+    pool are skipped.  Page "Day-0 Adaptation of Trillion-Parameter MoE
+    Models on Domestic GPUs", section 3 item (2) (paged layout); page
+    "Day-0 Adaptation of Ultra-Large-Scale MoE Models on Heterogeneous AI
+    Accelerators", section 4 (the written layout is the read layout)."""
+    rows = pool.reshape(-1, pool.shape[-1])
+    bt = np.asarray(block_table)
+    n_seq, max_blocks = bt.shape
+    n_rows = rows.shape[0]
+    for i in range(len(seq)):
+        b, p = int(seq[i]), int(pos[i])
+        if b < 0 or b >= n_seq or p < 0 or p // block_size >= max_blocks:
+            continue
+        blk = int(bt[b, p // block_size])
+        r = blk * block_size + p % block_size
+        if blk < 0 or r >= n_rows:
+            continue
+        rows[r, :new.shape[1]] = new[i]
+
+
 def decode_step(case, K=None):
     """The whole decode path on a host case from dsa_synth: scores, Top-K, attention."""
     wl = case.wl

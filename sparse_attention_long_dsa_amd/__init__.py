@@ -20,7 +20,8 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
-SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_latent.hip"]
+SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_latent.hip",
+           "cache_write.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # keep packed-fp32 instructions out of the generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -94,10 +95,11 @@ def lib():
         L.dsa_sparse_attn_decode_workspace_size.restype = sz
         L.dsa_sparse_attn_decode.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
         for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode,
-                  L.dsa_sparse_attn_prefill):
+                  L.dsa_sparse_attn_prefill, L.dsa_cache_write):
             f.restype = i32
         _lib = L
     return _lib
@@ -264,6 +266,25 @@ def sparse_attn_prefill(cache: Cache, q, idx, seq: int, pos0: int, sm_scale: flo
                                          K, seq, pos0, float(sm_scale), out.data_ptr(), _ptr(lse),
                                          _stream(stream)), "dsa_sparse_attn_prefill")
     return out, lse
+
+
+def cache_write(cache: Cache, seq, pos, kv_new, k_idx_new, v_new=None, stream=None):
+    """dsa_cache_write: store new tokens' rows into the paged pools in place.
+
+    seq, pos: int32 [n]; kv_new: bf16 [n, d_qk]; k_idx_new: bf16 [n, d_idx];
+    v_new: bf16 [n, d_v] exactly when the cache has a separate V pool."""
+    import torch
+
+    _need(seq, torch.int32, "seq")
+    _need(pos, torch.int32, "pos")
+    _need(kv_new, torch.bfloat16, "kv_new")
+    _need(k_idx_new, torch.bfloat16, "k_idx_new")
+    if v_new is not None:
+        _need(v_new, torch.bfloat16, "v_new")
+    n = seq.shape[0]
+    _check(lib().dsa_cache_write(ctypes.byref(cache.c), seq.data_ptr(), pos.data_ptr(), n,
+                                 kv_new.data_ptr(), _ptr(v_new), k_idx_new.data_ptr(),
+                                 _stream(stream)), "dsa_cache_write")
 
 
 class DecodeStep:

@@ -125,3 +125,22 @@ def test_attention_validation(L):
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE + 4, None, FAKE, ws, None) == 3
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE + 4, ws, None) == 3
     assert pre(ctypes.byref(c), FAKE + 2, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 3
+
+
+def test_cache_write_validation(L):
+    f = L.dsa_cache_write
+    c = cache()
+    assert f(ctypes.byref(c), FAKE, FAKE, 4, FAKE, None, FAKE, None) == 5     # well formed
+    assert f(ctypes.byref(c), FAKE, FAKE, 0, FAKE, None, FAKE, None) == 5     # device checked first
+    assert f(None, FAKE, FAKE, 4, FAKE, None, FAKE, None) == 1
+    assert f(ctypes.byref(c), None, FAKE, 4, FAKE, None, FAKE, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, 4, None, None, FAKE, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 1     # v_new without a V pool
+    sep = cache(v=FAKE, v_row_stride=64, d_qk=64, d_v=64, kv_row_stride=64)
+    assert f(ctypes.byref(sep), FAKE, FAKE, 4, FAKE, None, FAKE, None) == 1   # V pool needs v_new
+    assert f(ctypes.byref(sep), FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 5
+    assert f(ctypes.byref(c), FAKE, FAKE, -1, FAKE, None, FAKE, None) == 2
+    assert f(ctypes.byref(cache(kv_row_stride=500)), FAKE, FAKE, 4, FAKE, None, FAKE, None) == 2
+    assert f(ctypes.byref(cache(d_qk=570, kv_row_stride=576)), FAKE, FAKE, 4, FAKE, None, FAKE,
+             None) == 3
+    assert f(ctypes.byref(c), FAKE, FAKE, 4, FAKE + 8, None, FAKE, None) == 3  # alignment

@@ -209,3 +209,93 @@ def test_topk_causal_rows():
     got = dsa.topk(torch.from_numpy(scores).cuda(), 128, causal_base=0)
     want = oracle.topk(scores, np.arange(1, T + 1, dtype=np.int32), 128)
     np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+# ----------------------------------------------------------------------------- cache write
+
+def _bf16_rows(rng, n, d):
+    x = torch.from_numpy(rng.normal(size=(n, d)).astype(np.float32)).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+def _cache_write_case(wl, seed):
+    say(f"[cache write] {wl.name}")
+    rng = np.random.default_rng(seed)
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    cap = wl.max_blocks * wl.block_size
+    own = [nb * wl.block_size for nb in wl.blocks_per_seq]  # slots of each sequence's own blocks
+    # distinct slots of both sequences, plus tokens the call must skip
+    picks = [(0, int(p)) for p in rng.choice(own[0], 40, replace=False)] + \
+            [(1, int(p)) for p in rng.choice(own[1], 40, replace=False)]
+    picks += [(2, 0), (-1, 3), (0, -5), (1, cap)]
+    seq = np.array([b for b, _ in picks], np.int32)
+    pos = np.array([p for _, p in picks], np.int32)
+    n = len(picks)
+    kv_new = _bf16_rows(rng, n, wl.d_qk)
+    kidx_new = _bf16_rows(rng, n, wl.d_idx)
+    v_new = _bf16_rows(rng, n, wl.d_v) if wl.separate_v else None
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    dsa.cache_write(cache, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                    torch.from_numpy(kv_new.view(np.int16)).view(torch.bfloat16).cuda(),
+                    torch.from_numpy(kidx_new.view(np.int16)).view(torch.bfloat16).cuda(),
+                    None if v_new is None else
+                    torch.from_numpy(v_new.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    oracle.cache_write(hc.kv, hc.block_table, wl.block_size, seq, pos, kv_new)
+    oracle.cache_write(hc.k_idx, hc.block_table, wl.block_size, seq, pos, kidx_new)
+    if v_new is not None:
+        oracle.cache_write(hc.v, hc.block_table, wl.block_size, seq, pos, v_new)
+
+    def host_bits(t):
+        return t.reshape(-1, t.shape[-1]).view(torch.int16).cpu().numpy().view(np.uint16)
+
+    np.testing.assert_array_equal(host_bits(dc.kv), hc.kv)
+    np.testing.assert_array_equal(host_bits(dc.k_idx), hc.k_idx)
+    if v_new is not None:
+        np.testing.assert_array_equal(host_bits(dc.v), hc.v)
+    say("   ok: pools bit-identical to the oracle's")
+
+
+def test_cache_write_latent_pools():
+    _cache_write_case(dsa_synth.latent("cw_latent", "decode", [300, 700], seed=41, topk=256), 41)
+
+
+def test_cache_write_separate_v_pool():
+    _cache_write_case(dsa_synth.small_mqa("cw_small", "decode", [100, 250], seed=42, topk=64,
+                                          block_size=16), 42)
+
+
+def test_cache_written_rows_are_what_decode_reads():
+    # a cache filled token by token through dsa_cache_write (shuffled order)
+    # from the logical rows gives the decode step the oracle computes on the
+    # generator's pool
+    wl = dsa_synth.latent("cw_roundtrip", "decode", [900, 2100], seed=43, topk=512)
+    say(f"[cache write -> decode] {wl.name}")
+    hc = dsa_synth.host_case(wl)
+    dc = dsa_synth.device_case(wl)
+    bs = wl.block_size
+    seq, pos = [], []
+    for b, L in enumerate(wl.seq_lens):
+        seq += [b] * L
+        pos += list(range(L))
+    seq, pos = np.array(seq, np.int32), np.array(pos, np.int32)
+    perm = np.random.default_rng(43).permutation(len(seq))
+    seq, pos = seq[perm], pos[perm]
+    rows = hc.block_table[seq, pos // bs] * bs + pos % bs
+    dc.kv.fill_(float("nan"))
+    dc.k_idx.fill_(float("nan"))
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dsa.cache_write(cache, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                    dev(hc.kv[rows]), dev(hc.k_idx[rows]))
+    step = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
+    step(dc.q, dc.q_idx, dc.w, wl.sm_scale)
+    torch.cuda.synchronize()
+    sc, idx, out, lse = oracle.decode_step(hc)
+    np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
+    mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name)
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")

@@ -331,3 +331,60 @@ def test_latent_value_is_prefix_of_key_row(oracle_lib):
     b, lb = oracle_lib.sparse_attn(kb, np.ascontiguousarray(kb[:, :16]), bt, 4, q, [0], sel, 0.2)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
+
+
+# ----------------------------------------------------------------------------- cache write
+
+def test_hand_worked_cache_write(oracle_lib):
+    g = json.load(open(GOLDEN))["cache_write"]
+    pool = np.zeros((g["pool_rows"], 2), np.uint16)
+    toks = g["tokens"]
+    oracle_lib.cache_write(pool, np.array(g["block_table"], np.int32), g["block_size"],
+                           [t["seq"] for t in toks], [t["pos"] for t in toks],
+                           np.array([t["row"] for t in toks], np.uint16))
+    want = np.zeros_like(pool)
+    for r, row in g["written_rows"].items():
+        want[int(r)] = row
+    np.testing.assert_array_equal(pool, want)
+
+
+def test_cache_write_then_attention_reads_the_same_rows(oracle_lib):
+    """Rows written token by token through a shuffled block table, then read
+    back by the oracle's attention (C code, its own gather), give the same
+    result as the rows laid out contiguously with an identity table."""
+    rng = np.random.default_rng(31)
+    L, bs, d_qk, d_v, H = 23, 4, 24, 16, 2
+    blocks = (L + bs - 1) // bs
+    bt, n_blocks = random_table(rng, 2, blocks, extra=2)
+    k = bf16_bits_round(rng.normal(size=(L, d_qk)))
+    v = bf16_bits_round(rng.normal(size=(L, d_v)))
+    kpool = np.full((n_blocks * bs, d_qk), 0x7fc0, np.uint16)   # NaN: a stray read shows
+    vpool = np.full((n_blocks * bs, d_v), 0x7fc0, np.uint16)
+    order = rng.permutation(L)                                  # any write order
+    seq = np.ones(L, np.int32)
+    oracle_lib.cache_write(kpool, bt, bs, seq, order, k[order])
+    oracle_lib.cache_write(vpool, bt, bs, seq, order, v[order])
+    q = bf16_bits_round(rng.normal(size=(L, H, d_qk)))
+    idx = np.tile(np.arange(L, dtype=np.int32), (L, 1))
+    for t in range(L):
+        idx[t, t + 1:] = -1
+    got, lg = oracle_lib.sparse_attn(kpool, vpool, bt, bs, q, np.ones(L, np.int32), idx, 0.3)
+    ident = np.arange(blocks, dtype=np.int32).reshape(1, blocks)
+    kc = np.zeros((blocks * bs, d_qk), np.uint16)
+    vc = np.zeros((blocks * bs, d_v), np.uint16)
+    kc[:L], vc[:L] = k, v
+    want, lw = oracle_lib.sparse_attn(kc, vc, ident, bs, q, np.zeros(L, np.int32), idx, 0.3)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(lg, lw)
+    # sequence 0's blocks and the spare blocks were not touched
+    touched = {int(b) * bs + s for b in bt[1] for s in range(bs)}
+    for r in range(n_blocks * bs):
+        if r not in touched:
+            assert (kpool[r] == 0x7fc0).all() and (vpool[r] == 0x7fc0).all()
+
+
+def test_cache_write_skips_tokens_outside_the_table(oracle_lib):
+    pool = np.zeros((8, 1), np.uint16)
+    bt = np.array([[0, 1], [2, 3]], np.int32)
+    oracle_lib.cache_write(pool, bt, 2, [2, -1, 0, 0], [0, 0, -1, 4], np.ones((4, 1), np.uint16))
+    assert not pool.any()
