@@ -84,7 +84,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 
 // Launches the latent-row kernel (128 heads on a 576-wide row, V = its
 // first 512 columns), and the split merge when plan.n_splits > 1.
-void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
+__attribute__((visibility("hidden"))) void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
                    int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
                    uint16_t* out, float* lse, float* part_o, float* part_lse, SplitPlan plan,
                    hipStream_t stream);
