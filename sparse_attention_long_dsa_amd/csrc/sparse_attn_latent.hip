@@ -24,7 +24,8 @@ namespace {
 //        magnitudes in [2^-17, 65504].  P goes through a small LDS buffer
 //        from the wave that computed it to all four.
 // Softmax statistics stay with the head owner; the exponent base of a head
-// is its maximum over the first tile and never moves, so O^T (128 heads x
+// is its maximum over the first tile that holds a kept row and never moves
+// (negative indices are skipped, so a tile can hold none), so O^T (128 heads x
 // 128 columns fp32 per wave, in the accumulation registers) is never
 // rescaled.  A block whose later logits pass that base by more than 2^15 in
 // weight (the fp16 range) runs its tiles again with the true maximum as the
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kBufs][kBufBytes / 2];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kPElems];
   __shared__ int32_t trows[kMaxTiles * kTile];
+  __shared__ uint32_t tvalid[kMaxTiles];  // per tile: slots that hold a kept row
   __shared__ float head_l[kHeads], head_lse[kHeads];
 
   // blocks of one query share an XCD (same block id modulo 8)
@@ -174,12 +176,37 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   const int t_begin = split * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // physical rows of this block's kept positions; a padded slot repeats the
-  // first kept row (finite data, weight 0)
-  const int32_t row0 = count > 0 ? (int32_t)paged_row(bt_row, bs, sel[0]) : 0;
-  for (int r = threadIdx.x; r < (t_end - t_begin) * kTile; r += kThreads) {
-    const int g = t_begin * kTile + r;
-    trows[r] = g < count ? (int32_t)paged_row(bt_row, bs, sel[g]) : row0;
+  // Physical rows of this block's kept positions, and per tile a bit mask of
+  // the slots that hold one (slot < count and index >= 0: negative indices
+  // are skipped).  Other slots read the row of position 0 (always a cached
+  // token: finite data) with weight 0.  All index loads of a thread go out
+  // together, then all block-table loads: two memory round trips.
+  {
+    constexpr int kPer = kMaxTiles * kTile / kThreads;
+    const int n_rows = (t_end - t_begin) * kTile;
+    const int32_t row_safe = (int32_t)bt_row[0] * bs;
+    int32_t pos_r[kPer], blk_r[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = (int)threadIdx.x + kThreads * i;
+      const int g = t_begin * kTile + r;
+      pos_r[i] = r < n_rows && g < count ? sel[g] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) blk_r[i] = pos_r[i] >= 0 ? bt_row[pos_r[i] / bs] : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = (int)threadIdx.x + kThreads * i;
+      const bool ok = pos_r[i] >= 0;
+      if (r < n_rows) trows[r] = ok ? blk_r[i] * bs + pos_r[i] % bs : row_safe;
+      // slots 64 w' .. 64 w' + 63 of this wave: two tiles' masks
+      const uint64_t m = __ballot(ok);
+      const int s0 = kThreads * i + kWave * wave;
+      if (lane == 0 && s0 < n_rows) {
+        tvalid[s0 / kTile] = (uint32_t)m;
+        tvalid[s0 / kTile + 1] = (uint32_t)(m >> 32);
+      }
+    }
   }
 
   // q as the B operand of S^T: head `head`, dims 16 ks + 8 half .. + 7
@@ -249,11 +276,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
 
   // weights of tokens 16 ks + 8 half .. + 7 of head `head` (fp16, packed)
   auto weights_half = [&](const f32x16& sv, int ks, float& psum) {
+    // before the first kept row the base is still -inf: every weight is 0
+    const float m_use = m_base == -INFINITY ? 0.f : m_base;
     u32x4 ph;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w], scale_log2, -m_base));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w + 1], scale_log2, -m_base));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w], scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w + 1], scale_log2, -m_use));
       psum += p0 + p1;
       ph[w] = pack_f16x2(p0, p1);
     }
@@ -333,12 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           if (next && ks < kWaveBlocks) load_block(ks);
         }
         mfma_result_fence(s);
-        const int g0 = t * kTile;
-        const bool full = g0 + kTile <= count;
-        if (!full) {
+        const uint32_t vm = tvalid[t - t_begin];
+        if (vm != 0xffffffffu) {
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (g0 + acc_token(v, half) >= count) s[v] = -INFINITY;
+            if (!((vm >> acc_token(v, half)) & 1u)) s[v] = -INFINITY;
         }
       } else {
 #pragma unroll

@@ -299,3 +299,31 @@ def test_cache_written_rows_are_what_decode_reads():
     np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
     mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name)
     say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+
+
+# ----------------------------------------------------------------------------- index holes
+
+def test_attention_skips_negative_indices():
+    # entries < 0 inside the first min(K, n) slots are skipped; a row with no
+    # kept entry gives out = 0, lse = -inf
+    wl = dsa_synth.latent("holes", "decode", [700, 3000, 5000], seed=27, topk=512)
+    say(f"[holes] {wl.name}")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    _, idx, _, _ = oracle.decode_step(hc)
+    rng = np.random.default_rng(27)
+    holes = idx.copy()
+    holes[rng.random(holes.shape) < 0.3] = -1      # random holes
+    holes[1, :40] = -1                             # a first tile with nothing kept
+    holes[2, :] = -1                               # nothing kept at all
+    out, lse = oracle.sparse_attn(hc.kv, hc.v, hc.block_table, wl.block_size, hc.q, hc.q_seq,
+                                  holes, wl.sm_scale, d_v=wl.d_v)
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    o, l = dsa.sparse_attn_decode(cache, dc.q, torch.from_numpy(holes).cuda(), wl.sm_scale)
+    torch.cuda.synchronize()
+    mx, mn = assert_attention(o, None, out, None, wl.name)
+    lg = l.cpu().numpy()
+    assert np.all(np.isneginf(lg[2]))
+    np.testing.assert_allclose(lg[:2], lse[:2], atol=1e-2)
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
