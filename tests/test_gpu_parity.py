@@ -88,6 +88,14 @@ def test_latent_decode_peaked_softmax():
     check_decode(wl, rel=True)
 
 
+def test_latent_decode_wide_batch():
+    # more than 1024 sequences: the index score takes its per-(sequence,
+    # chunk) kernel instead of the token-balanced one
+    lens = [int(x) for x in np.random.default_rng(28).integers(1, 300, size=1100)]
+    wl = dsa_synth.latent("latent_wide", "decode", lens, seed=28, topk=64, block_size=16)
+    check_decode(wl)
+
+
 def test_block_table_invariance():
     a = dsa_synth.latent("inv", "decode", [3000, 20000], seed=25, topk=512)
     b = dsa_synth.latent("inv", "decode", [3000, 20000], seed=25, topk=512, table_seed=99)
@@ -126,6 +134,11 @@ def test_latent_prefill():
 def test_latent_prefill_chunk():
     check_prefill(dsa_synth.latent("prefill_chunk", "prefill", [700], seed=32, topk=200),
                   pos0=300, T=400)
+
+
+def test_latent_prefill_block_size_16():
+    check_prefill(dsa_synth.latent("prefill_bs16", "prefill", [500], seed=37, topk=100,
+                                   block_size=16), pos0=37, T=463)
 
 
 def test_latent_prefill_chunk_past_8192_keys():
