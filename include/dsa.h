@@ -40,8 +40,10 @@
  *       attention (H, d_qk, d_v) = (128, 576, 512) with V the first 512
  *                 columns of each K row (cache->v == NULL), or (8, 64, 64)
  *                 with a separate V pool;
- *       1 <= K <= 2048; any lengths; block_size a multiple of 16 for
- *       dsa_index_score, any block_size >= 1 for the other calls.
+ *       1 <= K <= 2048; any lengths, except that one dsa_index_score
+ *       prefill call takes at most 1048560 queries (chunk longer prefills);
+ *       block_size a multiple of 16 for dsa_index_score, any block_size >= 1
+ *       for the other calls.
  *   - Precision of attention: q.K in bf16 with fp32 accumulation.  In the
  *     (128, 576, 512) family the P.V product runs in fp16 with fp32
  *     accumulation: the weights carry 11 significant bits and the values are
