@@ -31,8 +31,10 @@ inline SplitPlan plan_splits(int B, int head_groups, int K) {
 // about 256 workgroups run.
 inline SplitPlan plan_splits_latent(int B, int K) {
   const int tiles = (K + kTile - 1) / kTile;
+  // about one workgroup per CU, but at least 4 tiles a split: a split's
+  // fixed cost (its q and row lookups, its partial result) is worth ~2 tiles
   int want = (256 + B - 1) / B;
-  want = std::max(1, std::min(want, tiles));
+  want = std::max(1, std::min(want, std::max(1, tiles / 4)));
   const int tps = (tiles + want - 1) / want;
   return SplitPlan{(tiles + tps - 1) / tps, tps};
 }
