@@ -48,7 +48,9 @@
  *     (128, 576, 512) family the P.V product runs in fp16 with fp32
  *     accumulation: the weights carry 11 significant bits and the values are
  *     converted from bf16, exactly for magnitudes in [2^-17, 65504], so value
- *     entries must stay within the fp16 range (|v| <= 65504).  The (8, 64, 64)
+ *     entries must stay within the fp16 range (|v| <= 65504); the decode
+ *     split partials (each split's normalised output) are kept in fp16 too,
+ *     while the log-sum-exp merge runs in fp32.  The (8, 64, 64)
  *     family carries each weight as a bf16 pair (16 bits) and has no range
  *     limit beyond bf16's.
  */

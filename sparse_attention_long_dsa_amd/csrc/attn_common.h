@@ -41,11 +41,21 @@ inline SplitPlan plan_splits_latent(int B, int K) {
 
 namespace {
 
+// Four consecutive partial values as fp32: from fp32 partials, or from fp16
+// ones (8 bytes).
+__device__ __forceinline__ f32x4 load_part4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load_part4(const uint16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  const f16x2 a = __builtin_bit_cast(f16x2, u.x), b = __builtin_bit_cast(f16x2, u.y);
+  return f32x4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
 // Log-sum-exp merge of the split-K partial results: one workgroup per
-// (query, head); thread t owns value dims 4 t .. 4 t + 3 (16-byte loads,
-// 8-byte stores), looping when D_V > 4 * 128.
-template <int D_V>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+// (query, head); thread t owns value dims 4 t .. 4 t + 3 (16-byte loads of
+// fp32 partials or 8-byte loads of fp16 ones, 8-byte stores), looping when
+// D_V > 4 * 128.
+template <int D_V, typename PT>
+__global__ __launch_bounds__(128) void attn_combine_kernel(const PT* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            int n_splits, int H,
                                                            uint16_t* __restrict__ out,
@@ -67,7 +77,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int d = 4 * (threadIdx.x + 128 * e);
-      if (d < D_V) acc[e] += wgt * *(const f32x4*)(part_o + p * D_V + d);
+      if (d < D_V) acc[e] += wgt * load_part4(part_o + p * D_V + d);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -88,7 +98,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 // first 512 columns), and the split merge when plan.n_splits > 1.
 __attribute__((visibility("hidden"))) void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
                    int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
-                   uint16_t* out, float* lse, float* part_o, float* part_lse, SplitPlan plan,
+                   uint16_t* out, float* lse, uint16_t* part_o, float* part_lse, SplitPlan plan,
                    hipStream_t stream);
 
 }  // namespace dsa

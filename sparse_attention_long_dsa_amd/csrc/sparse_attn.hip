@@ -364,15 +364,24 @@ void launch_attn(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* i
                      idx, n_q, K, H, head_groups, seq_lens, seq, pos0, plan.tiles_per_split,
                      sm_scale * kLog2e, out, lse, part_o, part_lse, plan.n_splits);
   if (plan.n_splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel<D_V>, dim3(n_q * H), dim3(128), 0, stream, part_o,
+    hipLaunchKernelGGL((attn_combine_kernel<D_V, float>), dim3(n_q * H), dim3(128), 0, stream, part_o,
                        part_lse, plan.n_splits, H, out, lse);
 }
 
 int head_groups_of(int H) { return H == 128 ? 2 : 1; }
 
 // Split plan of the decode call (also what sizes its workspace).
+bool latent_shape(int H, int d_v) { return H == 128 && d_v == 512; }
+
 SplitPlan decode_plan(int B, int H, int K, int d_v) {
-  return (H == 128 && d_v == 512) ? plan_splits_latent(B, K) : plan_splits(B, head_groups_of(H), K);
+  return latent_shape(H, d_v) ? plan_splits_latent(B, K) : plan_splits(B, head_groups_of(H), K);
+}
+
+// Bytes of the partial outputs in the workspace (256-byte rounded): fp16 for
+// the latent family, fp32 for the other.
+size_t part_o_bytes(int B, int H, int d_v, SplitPlan p) {
+  const size_t elems = (size_t)B * p.n_splits * H * d_v;
+  return (elems * (latent_shape(H, d_v) ? 2 : 4) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -384,8 +393,7 @@ extern "C" size_t dsa_sparse_attn_decode_workspace_size(int32_t B, int32_t H, in
   if (B < 1 || H < 1 || K < 1 || d_v < 1) return 0;
   const SplitPlan p = decode_plan(B, H, K, d_v);
   if (p.n_splits == 1) return 0;
-  const size_t o = (size_t)B * p.n_splits * H * d_v * 4;
-  return (o + 255) / 256 * 256 + (size_t)B * p.n_splits * H * 4;
+  return part_o_bytes(B, H, d_v, p) + (size_t)B * p.n_splits * H * 4;
 }
 
 extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, const uint16_t* q,
@@ -405,16 +413,14 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
   st = check_device();
   if (st != DSA_OK) return st;
   const SplitPlan plan = decode_plan(B, H, K, cache->d_v);
-  float* part_o = (float*)workspace;
-  float* part_lse = need ? (float*)((char*)workspace +
-                                    ((size_t)B * plan.n_splits * H * cache->d_v * 4 + 255) / 256 * 256)
-                         : nullptr;
+  float* part_lse =
+      need ? (float*)((char*)workspace + part_o_bytes(B, H, cache->d_v, plan)) : nullptr;
   if (fam == kLatent)
-    launch_latent(cache, q, idx, B, K, cache->seq_lens, 0, 0, sm_scale, out, lse, part_o,
-                  part_lse, plan, stream);
+    launch_latent(cache, q, idx, B, K, cache->seq_lens, 0, 0, sm_scale, out, lse,
+                  (uint16_t*)workspace, part_lse, plan, stream);
   else
     launch_attn<1, 64, 64, true>(cache, q, idx, B, H, K, cache->seq_lens, 0, 0, sm_scale, out,
-                                 lse, part_o, part_lse, plan, stream);
+                                 lse, (float*)workspace, part_lse, plan, stream);
   return launch_status();
 }
 

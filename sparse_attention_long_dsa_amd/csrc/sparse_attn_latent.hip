@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     int max_blocks, int bs, const uint16_t* __restrict__ q, const int32_t* __restrict__ idx,
     int n_q, int K, const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0,
     int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kBufs][kBufBytes / 2];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kPElems];
   __shared__ int32_t trows[kMaxTiles * kTile];
@@ -439,14 +439,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       const float lh = head_l[h];
       const float inv_l = lh > 0.f ? 1.f / lh : 0.f;
       const int64_t pidx = ((int64_t)qi * n_splits + split) * kHeads + h;
-      float* prow = part_o + pidx * kDv + c_wave + 4 * half;
+      // fp16 partials (normalised, 11 significant bits): half the bytes of
+      // fp32 to write here and to read in the merge
+      uint16_t* prow = part_o + pidx * kDv + c_wave + 4 * half;
 #pragma unroll
       for (int d = 0; d < kDVB; ++d)
 #pragma unroll
         for (int bq = 0; bq < 4; ++bq)
-          *(f32x4*)(prow + 32 * d + 8 * bq) =
-              f32x4{o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l,
-                    o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l};
+          *(uint2*)(prow + 32 * d + 8 * bq) =
+              make_uint2(pack_f16x2(o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l),
+                         pack_f16x2(o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l));
     }
     if (half == 0) part_lse[((int64_t)qi * n_splits + split) * kHeads + head] = lse_val;
   }
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
 
 void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
                    int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
-                   uint16_t* out, float* lse, float* part_o, float* part_lse, SplitPlan plan,
+                   uint16_t* out, float* lse, uint16_t* part_o, float* part_lse, SplitPlan plan,
                    hipStream_t stream) {
   const int64_t blocks = ((int64_t)n_q + 7) / 8 * 8 * plan.n_splits;
   hipLaunchKernelGGL(latent::sparse_attn_latent_kernel, dim3((unsigned)blocks),
@@ -466,7 +468,7 @@ void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t*
                      plan.tiles_per_split, sm_scale * kLog2e, out, lse, part_o, part_lse,
                      plan.n_splits);
   if (plan.n_splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel<latent::kDv>, dim3(n_q * latent::kHeads), dim3(128), 0,
+    hipLaunchKernelGGL((attn_combine_kernel<latent::kDv, uint16_t>), dim3(n_q * latent::kHeads), dim3(128), 0,
                        stream, part_o, part_lse, plan.n_splits, latent::kHeads, out, lse);
 }
 
