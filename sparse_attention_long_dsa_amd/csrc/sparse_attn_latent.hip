@@ -176,6 +176,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   const int t_begin = split * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
+  // q as the B operand of S^T (issued first: its loads fly during the row
+  // lookups below): head `head`, dims 16 ks + 8 half .. + 7
+  bf16x8 qf[kKS];
+  {
+    const uint16_t* qrow = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 16 * ks));
+  }
   // Physical rows of this block's kept positions, and per tile a bit mask of
   // the slots that hold one (slot < count and index >= 0: negative indices
   // are skipped).  Other slots read the row of position 0 (always a cached
@@ -209,19 +217,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     }
   }
 
-  // q as the B operand of S^T: head `head`, dims 16 ks + 8 half .. + 7
-  bf16x8 qf[kKS];
-  {
-    const uint16_t* qrow = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * half;
+  // Consume q here, so that the compiler waits for these loads before the
+  // tile loop.  Otherwise it counts them as possibly in flight inside the
+  // loop and its waits there (which also cover the direct-to-LDS tile loads
+  // it does not see) would drain the next tile's loads every tile.
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 16 * ks));
-    // Consume q here, so that the compiler waits for these loads before the
-    // tile loop.  Otherwise it counts them as possibly in flight inside the
-    // loop and its waits there (which also cover the direct-to-LDS tile
-    // loads it does not see) would drain the next tile's loads every tile.
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
+  for (int ks = 0; ks < kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
   __syncthreads();
 
   // Loads of a tile: wave w brings rows 8 w .. 8 w + 7, one wave load per
