@@ -413,45 +413,57 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     head_lse[head] = lse_val;
   }
   __syncthreads();
-  // lane holds head 32 hb + lane % 32 and value columns
-  // c_wave + 32 d + 8 (v / 4) + 4 half + v % 4
-  if (n_splits == 1) {
+  // Lane holds head 32 hb + lane % 32 and value columns
+  // c_wave + 32 d + 8 (v / 4) + 4 half + v % 4.  The normalised rows go out
+  // through LDS (the tile buffers are free now), 64 heads at a time, so that
+  // every global store writes whole 1 KB rows: written straight from the
+  // accumulator layout, each store instruction would touch 32 rows with 16
+  // bytes each.  The final output is bf16; split partials are fp16 (11
+  // significant bits: half the bytes of fp32 to write here and to read in the
+  // merge).
+  const bool final_out = n_splits == 1;
+  uint16_t* const dst = final_out
+                            ? out + (int64_t)qi * kHeads * kDv
+                            : part_o + ((int64_t)qi * n_splits + split) * kHeads * kDv;
+  constexpr int kStageRow = kDv + 8;  // elements: 1040-byte rows
+  constexpr int kStageHeads = 64;
+  static_assert(kStageHeads * kStageRow * 2 <= kBufs * kBufBytes, "stage fits the tile buffers");
+  uint16_t* const stage = &tiles[0][0];
 #pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) {
+  for (int r = 0; r < kHeads / kStageHeads; ++r) {
+    if (r > 0) __syncthreads();  // the previous round's rows have been read out
+#pragma unroll
+    for (int hh = 0; hh < kStageHeads / 32; ++hh) {
+      const int hb = (kStageHeads / 32) * r + hh;
       const int h = 32 * hb + (lane & 31);
       const float lh = head_l[h];
       const float inv_l = lh > 0.f ? 1.f / lh : 0.f;
-      uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kDv + c_wave + 4 * half;
+      uint16_t* srow = stage + (h - kStageHeads * r) * kStageRow + c_wave + 4 * half;
 #pragma unroll
       for (int d = 0; d < kDVB; ++d)
 #pragma unroll
         for (int bq = 0; bq < 4; ++bq) {
-          const uint32_t lo = pack_bf16x2(o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l);
-          const uint32_t hi =
-              pack_bf16x2(o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l);
-          *(uint2*)(orow + 32 * d + 8 * bq) = make_uint2(lo, hi);
+          const float x0 = o[hb][d][4 * bq] * inv_l, x1 = o[hb][d][4 * bq + 1] * inv_l;
+          const float x2 = o[hb][d][4 * bq + 2] * inv_l, x3 = o[hb][d][4 * bq + 3] * inv_l;
+          *(uint2*)(srow + 32 * d + 8 * bq) =
+              final_out ? make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3))
+                        : make_uint2(pack_f16x2(x0, x1), pack_f16x2(x2, x3));
         }
     }
-    if (lse && half == 0) lse[(int64_t)qi * kHeads + head] = lse_val;
-  } else {
+    __syncthreads();
+    constexpr int kChunks = kDv / 8;  // 16-byte chunks per row
 #pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) {
-      const int h = 32 * hb + (lane & 31);
-      const float lh = head_l[h];
-      const float inv_l = lh > 0.f ? 1.f / lh : 0.f;
-      const int64_t pidx = ((int64_t)qi * n_splits + split) * kHeads + h;
-      // fp16 partials (normalised, 11 significant bits): half the bytes of
-      // fp32 to write here and to read in the merge
-      uint16_t* prow = part_o + pidx * kDv + c_wave + 4 * half;
-#pragma unroll
-      for (int d = 0; d < kDVB; ++d)
-#pragma unroll
-        for (int bq = 0; bq < 4; ++bq)
-          *(uint2*)(prow + 32 * d + 8 * bq) =
-              make_uint2(pack_f16x2(o[hb][d][4 * bq] * inv_l, o[hb][d][4 * bq + 1] * inv_l),
-                         pack_f16x2(o[hb][d][4 * bq + 2] * inv_l, o[hb][d][4 * bq + 3] * inv_l));
+    for (int i = 0; i < kStageHeads * kChunks / kThreads; ++i) {
+      const int flat = kThreads * i + (int)threadIdx.x;
+      const int row = flat / kChunks, ch = flat % kChunks;
+      const u32x4 val = *(const u32x4*)(stage + row * kStageRow + 8 * ch);
+      *(u32x4*)(dst + (int64_t)(kStageHeads * r + row) * kDv + 8 * ch) = val;
     }
-    if (half == 0) part_lse[((int64_t)qi * n_splits + split) * kHeads + head] = lse_val;
+  }
+  if (final_out) {
+    if (lse && half == 0) lse[(int64_t)qi * kHeads + head] = lse_val;
+  } else if (half == 0) {
+    part_lse[((int64_t)qi * n_splits + split) * kHeads + head] = lse_val;
   }
 }
 
