@@ -65,19 +65,50 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const PT* __restrict_
   const int qh = blockIdx.x;  // qi * H + head
   const int qi = qh / H, head = qh % H;
   float m = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    m = fmaxf(m, part_lse[((int64_t)qi * n_splits + s) * H + head]);
   float wsum = 0.f;
   f32x4 acc[kPer] = {};
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
-    const float l = part_lse[p];
-    const float wgt = l == -INFINITY ? 0.f : __expf(l - m);
-    wsum += wgt;
+  constexpr int kMaxS = 16;
+  if (n_splits <= kMaxS) {
+    // every load of the workgroup goes out at once: one memory round trip
+    float l[kMaxS];
+    f32x4 v[kMaxS][kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int d = 4 * (threadIdx.x + 128 * e);
-      if (d < D_V) acc[e] += wgt * load_part4(part_o + p * D_V + d);
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < n_splits) {
+        const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
+        l[s] = part_lse[p];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int d = 4 * (threadIdx.x + 128 * e);
+          v[s][e] = d < D_V ? load_part4(part_o + p * D_V + d) : f32x4{};
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s)
+      if (s < n_splits) m = fmaxf(m, l[s]);
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < n_splits) {
+        const float wgt = l[s] == -INFINITY ? 0.f : __expf(l[s] - m);
+        wsum += wgt;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[e] += wgt * v[s][e];
+      }
+    }
+  } else {
+    for (int s = 0; s < n_splits; ++s)
+      m = fmaxf(m, part_lse[((int64_t)qi * n_splits + s) * H + head]);
+    for (int s = 0; s < n_splits; ++s) {
+      const int64_t p = ((int64_t)qi * n_splits + s) * H + head;
+      const float l = part_lse[p];
+      const float wgt = l == -INFINITY ? 0.f : __expf(l - m);
+      wsum += wgt;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int d = 4 * (threadIdx.x + 128 * e);
+        if (d < D_V) acc[e] += wgt * load_part4(part_o + p * D_V + d);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

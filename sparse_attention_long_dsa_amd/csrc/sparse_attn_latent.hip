@@ -158,9 +158,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   // blocks of one query share an XCD (same block id modulo 8)
   const int b = blockIdx.x;
   const int j = b >> 3;
-  const int qi = (j / n_splits) * 8 + (b & 7), split = j % n_splits;
-  if (qi >= n_q) return;
   const bool decode = seq_lens != nullptr;
+  // prefill rows grow with the position: the longest go first
+  const int qraw = (j / n_splits) * 8 + (b & 7), split = j % n_splits;
+  const int qi = decode ? qraw : n_q - 1 - qraw;
+  if (qi >= n_q || qi < 0) return;
   const int seq = decode ? qi : prefill_seq;
   const int n_cand = decode ? seq_lens[qi] : pos0 + qi + 1;
   const int count = min(K, n_cand);
@@ -176,8 +178,22 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   const int t_begin = split * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // q as the B operand of S^T (issued first: its loads fly during the row
-  // lookups below): head `head`, dims 16 ks + 8 half .. + 7
+  // Prologue loads, in the order that keeps the two dependent round trips
+  // (kept positions, then their block-table entries) off the q transfer:
+  // the index loads go first, then q (the B operand of S^T: head `head`,
+  // dims 16 ks + 8 half .. + 7), then the block-table loads, which wait
+  // only for the index loads (memory returns in issue order) while q is
+  // still in flight.
+  constexpr int kPer = kMaxTiles * kTile / kThreads;
+  const int n_rows = (t_end - t_begin) * kTile;
+  const int32_t row_safe = (int32_t)bt_row[0] * bs;
+  int32_t pos_r[kPer], blk_r[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = (int)threadIdx.x + kThreads * i;
+    const int g = t_begin * kTile + r;
+    pos_r[i] = r < n_rows && g < count ? sel[g] : -1;
+  }
   bf16x8 qf[kKS];
   {
     const uint16_t* qrow = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * half;
@@ -187,19 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   // Physical rows of this block's kept positions, and per tile a bit mask of
   // the slots that hold one (slot < count and index >= 0: negative indices
   // are skipped).  Other slots read the row of position 0 (always a cached
-  // token: finite data) with weight 0.  All index loads of a thread go out
-  // together, then all block-table loads: two memory round trips.
+  // token: finite data) with weight 0.
   {
-    constexpr int kPer = kMaxTiles * kTile / kThreads;
-    const int n_rows = (t_end - t_begin) * kTile;
-    const int32_t row_safe = (int32_t)bt_row[0] * bs;
-    int32_t pos_r[kPer], blk_r[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int r = (int)threadIdx.x + kThreads * i;
-      const int g = t_begin * kTile + r;
-      pos_r[i] = r < n_rows && g < count ? sel[g] : -1;
-    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) blk_r[i] = pos_r[i] >= 0 ? bt_row[pos_r[i] / bs] : 0;
 #pragma unroll
