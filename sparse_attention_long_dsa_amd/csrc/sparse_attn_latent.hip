@@ -434,6 +434,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   constexpr int kStageHeads = 64;
   static_assert(kStageHeads * kStageRow * 2 <= kBufs * kBufBytes, "stage fits the tile buffers");
   uint16_t* const stage = &tiles[0][0];
+  // a fresh copy of the thread index: otherwise the compiler keeps the
+  // prologue's thread-index sums alive across the tile loop (spilled to
+  // scratch, and reloaded between the stores below, each reload waiting for
+  // every store before it)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int r = 0; r < kHeads / kStageHeads; ++r) {
     if (r > 0) __syncthreads();  // the previous round's rows have been read out
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     constexpr int kChunks = kDv / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < kStageHeads * kChunks / kThreads; ++i) {
-      const int flat = kThreads * i + (int)threadIdx.x;
+      const int flat = kThreads * i + tid;
       const int row = flat / kChunks, ch = flat % kChunks;
       const u32x4 val = *(const u32x4*)(stage + row * kStageRow + 8 * ch);
       *(u32x4*)(dst + (int64_t)(kStageHeads * r + row) * kDv + 8 * ch) = val;
