@@ -59,6 +59,15 @@ def test_small_family_ragged_decode():
     check_decode(wl)
 
 
+def test_small_family_many_splits():
+    # Top-K 2048 over one or two sequences splits each query's kept rows
+    # over up to 64 workgroups: the split merge takes its general path
+    # (more splits than its register-resident fast path holds)
+    wl = dsa_synth.small_mqa("small_many_splits", "decode", [2100, 5000], seed=27, topk=2048,
+                             block_size=16)
+    check_decode(wl)
+
+
 def test_latent_decode_short_rows():
     # rows <= 16384 take the one-workgroup-per-row Top-K path
     wl = dsa_synth.latent("latent_short", "decode", [700, 2048, 2049, 5000, 9001], seed=22,
