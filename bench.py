@@ -67,13 +67,14 @@ def sha(paths):
     return h.hexdigest()
 
 
-def traffic_for(kernel_launches=1):
+def traffic_for(workload):
     """HBM bytes per index-score launch from the committed counter summary,
-    or None when missing or taken on a different kernel source."""
+    or None when missing, taken on another workload or on a different kernel
+    source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     t = json.load(open(TRAFFIC_FILE))
-    if t.get("source_sha256") != sha(INDEX_SRC):
+    if t.get("source_sha256") != sha(INDEX_SRC) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -298,9 +299,11 @@ def main():
     step_bytes, index_bytes = decode_bytes(wl)
     tok_s = wl.n_q / (ms * 1e-3)
     achieved = index_bytes / (idx_ms * 1e-3) / 1e9
-    traffic = traffic_for()
+    traffic = traffic_for(wl.name)
+    metric = ("decode tokens/s at 128K ctx (ragged 4K-128K, B=64, Top-K 2048)" if args.config == 4
+              else f"decode tokens/s ({wl.name}, Top-K {wl.topk})")
     res = {
-        "metric": "decode tokens/s at 128K ctx (ragged 4K-128K, B=64, Top-K 2048)",
+        "metric": metric,
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
