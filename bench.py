@@ -1,39 +1,65 @@
 """Benchmark of the DSA hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: index score -> Top-K ->
-sparse attention (decode: split-K + merge).  The default workload is the
+sparse attention (decode: split-K + merge).  The headline workload is the
 ragged long-context decode (64 sequences, lengths uniform on [4096, 131072],
 block size 64, 128 query heads on a 576-wide latent KV row, indexer 64 x 128,
-Top-K 2048); tokens/s counts one new token per sequence per step.  The 8192
-token causal prefill is measured too and reported in the "prefill" object.
+Top-K 2048); tokens/s counts one new token per sequence per step.  The other
+two full-size decode batches (32 x 32768 and 8 x 1048576) and the 8192-token
+causal prefill are measured in the same run and reported as sub-objects.
 
-Inputs are seeded synthetic data generated directly in HBM before timing.
+Timing: inputs are seeded synthetic data generated directly in HBM before
+timing.  Before every timed step a 512 MiB scratch buffer is written and
+another one read (outside the timed events), so no step finds the previous
+step's data in the caches, nor dirty lines of the flush to write back.
+Each step is bracketed by HIP events on the stream the kernels run on; the
+reported step time is the median over the timed steps.  A second pass of the
+same number of steps puts events between the calls for the per-call
+breakdown (the dominant kernel's time for the roofline comes from it).  The
+achievable HBM read bandwidth is measured by a streaming-read probe kernel
+and reported beside the 8 TB/s datasheet figure.
+
 Prints one JSON line (see --help for the options).
 
-Two helper modes feed the roofline's "traffic" figure:
+Helper modes for the roofline's "traffic" figure (rocprofv3 counters):
   bench.py --calibrate-copy     a plain 1 GiB device copy (counter calibration)
-  bench.py --write-traffic F W CF CW
+  bench.py --write-traffic KERNEL WORKLOAD F W CF CW
                                 fold rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                                 CSVs of the step (F, W) and of the copy (CF, CW)
-                                into profiles/index_score_decode_traffic.json
+                                into profiles/traffic_KERNEL.json
 """
 import argparse
+import ctypes
 import hashlib
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_decode_traffic.json")
-# the decode index kernel's sources (its file and the shared device helpers)
-INDEX_SRC = [os.path.join(ROOT, "sparse_attention_long_dsa_amd", "csrc", f)
-             for f in ("index_score.hip", "common.h")]
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s (datasheet)
+MFMA_BF16_PEAK_TF = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s (datasheet)
+# 256 CUs x 4 SIMDs x 1024 bf16 flop/clk x 2.4 GHz: the clock-derived dense
+# peak, slightly above the datasheet's rounded figure; prefill utilisation is
+# reported against it (the more conservative of the two)
+MFMA_BF16_CLOCK_PEAK_TF = 2516.6
+FLUSH_BYTES = 512 << 20         # scratch written before every timed step
+PROBE_BYTES = 2 << 30           # streaming-read probe buffer
+CSRC = os.path.join(ROOT, "sparse_attention_long_dsa_amd", "csrc")
+# kernel -> the sources its counter figures were taken on
+KERNEL_SOURCES = {
+    "index_score_decode": ["index_score.hip", "common.h"],
+    "sparse_attn_latent": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
+    "attn_combine": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
+    "topk": ["topk.hip", "common.h"],
+}
+
+
+def traffic_file(kernel):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
 
 
 def decode_bytes(wl):
@@ -53,6 +79,16 @@ def decode_bytes(wl):
     return step, index_launch
 
 
+def attn_bytes(wl):
+    """Algorithmic bytes of the decode attention: kept rows, q, the index
+    array, block-table entries of the kept rows, the output."""
+    L = wl.seq_lens
+    B, K = wl.n_q, wl.topk
+    kept = sum(min(K, x) for x in L)
+    return (kept * wl.d_qk * 2 + B * wl.H * wl.d_qk * 2 + B * K * 4 + kept * 4
+            + B * wl.H * wl.d_v * 2 + B * wl.H * 4)
+
+
 def prefill_flops(wl):
     T, K = wl.seq_lens[0], wl.topk
     pairs = T * (T + 1) // 2
@@ -67,82 +103,179 @@ def sha(paths):
     return h.hexdigest()
 
 
-def traffic_for(workload):
-    """HBM bytes per index-score launch from the committed counter summary,
-    or None when missing, taken on another workload or on a different kernel
-    source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when missing, taken on another workload or on different sources."""
+    f = traffic_file(kernel)
+    if not os.path.exists(f):
         return None
-    t = json.load(open(TRAFFIC_FILE))
-    if t.get("source_sha256") != sha(INDEX_SRC) or t.get("workload") != workload:
+    t = json.load(open(f))
+    srcs = [os.path.join(CSRC, s) for s in KERNEL_SOURCES[kernel]]
+    if t.get("source_sha256") != sha(srcs) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
 
-def time_decode(wl, steps, warmup, log):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def probe_lib():
+    import sparse_attention_long_dsa_amd as dsa
+
+    if not os.path.exists(dsa.PROBE_LIB):
+        raise RuntimeError(f"{dsa.PROBE_LIB} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(dsa.PROBE_LIB)
+    L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.hbm_read_probe.restype = ctypes.c_int
+    return L
+
+
+class Timer:
+    """Event-timed steps with a cache flush before each step.
+
+    The flush writes a 512 MiB scratch buffer (evicting L2 and the 256 MB
+    last-level cache) and then reads another 512 MiB buffer, so that the
+    written lines are written back before the step starts rather than
+    inside it; the step then finds only clean, unrelated lines cached.
+    `calls` is the list of the step's calls (each a no-argument function
+    that launches on the current stream).  Pass A brackets each whole step
+    with one event pair; pass B records an event between consecutive calls
+    for the breakdown."""
+
+    def __init__(self):
+        import torch
+
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.read_buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+        self.probe = probe_lib()
+        self.n_flush = 0
+
+    def flush(self):
+        self.n_flush += 1
+        self.flush_buf.fill_(self.n_flush & 0xFF)
+        rc = self.probe.hbm_read_probe(self.read_buf.data_ptr(), FLUSH_BYTES,
+                                       self.sink.data_ptr(), 4096,
+                                       ctypes.c_void_p(self.stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hbm_read_probe failed ({rc})")
+
+    def run(self, calls, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.flush()
+            ev[i][0].record(self.stream)
+            for c in calls:
+                c()
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        step_ms = [a.elapsed_time(b) for a, b in ev]
+        # pass B: per-call breakdown
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+               for _ in range(steps)]
+        for i in range(steps):
+            self.flush()
+            evb[i][0].record(self.stream)
+            for j, c in enumerate(calls):
+                c()
+                evb[i][j + 1].record(self.stream)
+        torch.cuda.synchronize()
+        per_call = [statistics.median(e[j].elapsed_time(e[j + 1]) for e in evb)
+                    for j in range(len(calls))]
+        return {"median_ms": statistics.median(step_ms), "min_ms": min(step_ms),
+                "max_ms": max(step_ms), "wall_ms_incl_flush": wall_ms, "per_call_ms": per_call}
+
+
+def bench_decode(n, timer, steps, warmup, log):
     import torch
 
     import dsa_synth
     import sparse_attention_long_dsa_amd as dsa
 
+    wl = dsa_synth.workload(n)
     t0 = time.time()
     dc = dsa_synth.device_case(wl, poison=False)
-    log(f"generated {wl.name} in HBM in {time.time() - t0:.1f}s")
+    log(f"generated {wl.name} (B={wl.n_q}, sum(L)={sum(wl.seq_lens)}) in HBM in "
+        f"{time.time() - t0:.1f}s")
     cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
-    step = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        step(dc.q, dc.q_idx, dc.w, wl.sm_scale)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        # the index-score kernel is launched on this stream; events bracket it
-        ev[i][0].record(stream)
-        dsa.index_score(cache, dc.q_idx, dc.w, dsa.DSA_DECODE, out=step.scores)
-        ev[i][1].record(stream)
-        dsa.topk(step.scores, wl.topk, n_valid=dc.seq_lens, out=step.idx,
-                 workspace=step.ws_topk)
-        dsa.sparse_attn_decode(cache, dc.q, step.idx, wl.sm_scale, out=step.out, lse=step.lse,
-                               workspace=step.ws_attn)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    idx_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return elapsed * 1e3 / steps, idx_ms
+    st = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
+    calls = [lambda: dsa.index_score(cache, dc.q_idx, dc.w, dsa.DSA_DECODE, out=st.scores),
+             lambda: dsa.topk(st.scores, wl.topk, n_valid=dc.seq_lens, out=st.idx,
+                              workspace=st.ws_topk),
+             lambda: dsa.sparse_attn_decode(cache, dc.q, st.idx, wl.sm_scale, out=st.out,
+                                            lse=st.lse, workspace=st.ws_attn)]
+    r = timer.run(calls, steps, warmup)
+    step_bytes, index_bytes = decode_bytes(wl)
+    ms = r["median_ms"]
+    idx_ms, topk_ms, attn_ms = r["per_call_ms"]
+    res = {
+        "workload": wl.name, "batch": wl.n_q, "sum_ctx": sum(wl.seq_lens),
+        "max_ctx": max(wl.seq_lens), "tokens_per_s": round(wl.n_q / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4), "ms_min": round(r["min_ms"], 4),
+        "ms_max": round(r["max_ms"], 4), "wall_ms_per_step_incl_flush": round(r["wall_ms_incl_flush"], 4),
+        "index_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4), "attn_ms": round(attn_ms, 4),
+        "algorithmic_bytes": step_bytes, "index_algorithmic_bytes": index_bytes,
+        "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "index_gbs": round(index_bytes / (idx_ms * 1e-3) / 1e9, 1),
+        "attn_gbs": round(attn_bytes(wl) / (attn_ms * 1e-3) / 1e9, 1),
+    }
+    del dc, cache, st, calls
+    torch.cuda.empty_cache()
+    return res, wl
 
 
-def time_prefill(wl, steps, warmup, log):
+def bench_prefill(timer, reps, warmup, log):
     import torch
 
     import dsa_synth
     import sparse_attention_long_dsa_amd as dsa
 
+    wl = dsa_synth.workload(3)
     dc = dsa_synth.device_case(wl, poison=False)
     cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
     T = wl.seq_lens[0]
-    step = dsa.PrefillStep(cache, T, wl.H, wl.topk, wl.d_v)
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        step(dc.q, dc.q_idx, dc.w, wl.sm_scale)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        dsa.index_score(cache, dc.q_idx, dc.w, dsa.DSA_PREFILL, out=step.scores)
-        ev[i][1].record(stream)
-        dsa.topk(step.scores, wl.topk, causal_base=0, out=step.idx, workspace=step.ws_topk)
-        ev[i][2].record(stream)
-        dsa.sparse_attn_prefill(cache, dc.q, step.idx, 0, 0, wl.sm_scale, out=step.out,
-                                lse=step.lse)
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(3)]
+    st = dsa.PrefillStep(cache, T, wl.H, wl.topk, wl.d_v)
+    calls = [lambda: dsa.index_score(cache, dc.q_idx, dc.w, dsa.DSA_PREFILL, q_seq=st.q_seq,
+                                     q_pos=st.q_pos, out=st.scores),
+             lambda: dsa.topk(st.scores, wl.topk, n_valid=st.n_valid, out=st.idx,
+                              workspace=st.ws_topk),
+             lambda: dsa.sparse_attn_prefill(cache, dc.q, st.q_seq, st.q_pos, st.idx,
+                                             wl.sm_scale, out=st.out, lse=st.lse)]
+    r = timer.run(calls, reps, warmup)
+    fi, fa = prefill_flops(wl)
+    ms = r["median_ms"]
+    parts = r["per_call_ms"]
+    peak = MFMA_BF16_CLOCK_PEAK_TF
+    res = {
+        "workload": wl.name, "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4), "reps": reps, "ms_min": round(r["min_ms"], 4),
+        "index_ms": round(parts[0], 4), "topk_ms": round(parts[1], 4),
+        "attn_ms": round(parts[2], 4), "flops": fi + fa, "mfma_peak_tflops": peak,
+        "mfma_util": round((fi + fa) / (ms * 1e-3) / 1e12 / peak, 4),
+        "attn_mfma_util": round(fa / (parts[2] * 1e-3) / 1e12 / peak, 4),
+        "index_mfma_util": round(fi / (parts[0] * 1e-3) / 1e12 / peak, 4)}
     # the cache write of the whole sequence: its own rows written back from a
     # contiguous copy (gathered untimed), so the pools end up unchanged
+    stream = torch.cuda.current_stream()
     pos = torch.arange(T, dtype=torch.int32, device=dc.kv.device)
     seq = torch.zeros_like(pos)
     bt = dc.block_table[0].long()
@@ -152,17 +285,16 @@ def time_prefill(wl, steps, warmup, log):
     dsa.cache_write(cache, seq, pos, kv_rows, kidx_rows)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
+    n_cw = 20
     a.record(stream)
-    for _ in range(reps):
+    for _ in range(n_cw):
         dsa.cache_write(cache, seq, pos, kv_rows, kidx_rows)
     b.record(stream)
     torch.cuda.synchronize()
-    cw_eager_ms = a.elapsed_time(b) / reps  # includes the Python launch of each call
-    # the same launches replayed from a captured HIP graph: device time only
-    g = torch.cuda.CUDAGraph()
+    cw_eager_ms = a.elapsed_time(b) / n_cw  # includes the Python launch of each call
+    g = torch.cuda.CUDAGraph()  # the same launches replayed from a HIP graph: device time
     with torch.cuda.graph(g):
-        for _ in range(reps):
+        for _ in range(n_cw):
             dsa.cache_write(cache, seq, pos, kv_rows, kidx_rows)
     g.replay()
     torch.cuda.synchronize()
@@ -170,12 +302,50 @@ def time_prefill(wl, steps, warmup, log):
     g.replay()
     b.record(stream)
     torch.cuda.synchronize()
-    cw_ms = a.elapsed_time(b) / reps
+    cw_ms = a.elapsed_time(b) / n_cw
     del g
     cw_bytes = 2 * T * 2 * (wl.d_qk + wl.d_idx) + 2 * T * 4 + T * 4
-    del dc, cache, step, kv_rows, kidx_rows
+    cw = {"workload": f"{wl.name}: {T} tokens' latent and indexer rows",
+          "ms": round(cw_ms, 4), "ms_eager": round(cw_eager_ms, 4), "bytes": cw_bytes,
+          "gbs": round(cw_bytes / (cw_ms * 1e-3) / 1e9, 1),
+          "frac": round(cw_bytes / (cw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dc, cache, st, kv_rows, kidx_rows, calls
     torch.cuda.empty_cache()
-    return elapsed * 1e3 / steps, parts, (cw_ms, cw_eager_ms, cw_bytes)
+    return res, cw
+
+
+def hbm_probe(log):
+    """Achievable HBM read bandwidth: the streaming-read probe over a 2 GiB
+    buffer, a few grid sizes, the best median of 5 reads each."""
+    import torch
+
+    L = probe_lib()
+    buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        times = []
+        for rep in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = L.hbm_read_probe(buf.data_ptr(), PROBE_BYTES, sink.data_ptr(), grid,
+                                  ctypes.c_void_p(stream.cuda_stream))
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm_read_probe failed ({rc})")
+            torch.cuda.synchronize()
+            if rep > 0:
+                times.append(a.elapsed_time(b))
+        gbs = PROBE_BYTES / (statistics.median(times) * 1e-3) / 1e9
+        log(f"hbm probe: grid {grid} x 256: {gbs:.0f} GB/s")
+        if best is None or gbs > best[0]:
+            best = (gbs, grid)
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "hbm_read_kernel (streaming read, 16 B a lane, 8 loads in flight)",
+            "bytes": PROBE_BYTES, "gbs": round(best[0], 1), "grid_blocks": best[1],
+            "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, budget_s, log):
@@ -194,9 +364,9 @@ def cpu_baseline(wl, budget_s, log):
         sc = oracle.index_score(k_idx, lbt, wl.block_size, q_idx, w, [0], [L - 1], ld=L)
         idx = oracle.topk(sc, [L], wl.topk)
         t1 = time.perf_counter()
-        _, _, kv, v = dsa_synth.host_sequence_pools(wl, b, kv_positions=idx[0])
+        table, kv, v = dsa_synth.host_kept_pool(wl, b, idx[0])
         t2 = time.perf_counter()
-        oracle.sparse_attn(kv, v, lbt, wl.block_size, q, [0], idx, wl.sm_scale, d_v=wl.d_v)
+        oracle.sparse_attn(kv, v, table, 1, q, [0], idx, wl.sm_scale, d_v=wl.d_v)
         spent += (t1 - t0) + (time.perf_counter() - t2)
         done += 1
         if spent >= budget_s:
@@ -204,6 +374,7 @@ def cpu_baseline(wl, budget_s, log):
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     log(f"cpu oracle: {done} sequences in {spent:.1f}s on {cores} threads")
     return {"value": done / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{done} of {wl.n_q} sequences of the same batch (first ones, "
                       f"{sum(wl.seq_lens[:done])} cached positions), one decode token each: "
                       f"index score over every position, Top-K, attention; input generation "
@@ -242,22 +413,22 @@ def _pmc_per_dispatch(csv_path, counter, name_part):
     return sum(vals.values()) / len(vals)
 
 
-def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cname="copyBuffer"):
-    """Fold two counter runs of the decode step and two of the plain copy into
-    profiles/index_score_decode_traffic.json (HBM bytes per launch).  `cname`
-    names the copy kernel (the runtime's device-to-device copy)."""
-    kname = "index_score_decode"
-    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kname)
-    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kname)
+def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                  cname="copyBuffer"):
+    """Fold two counter runs of a kernel and two of the plain copy into
+    profiles/traffic_KERNEL.json (HBM bytes per launch).  `cname` names the
+    copy kernel (the runtime's device-to-device copy)."""
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kernel)
     cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", cname)
     cw = _pmc_per_dispatch(copy_write_csv, "WRITE_SIZE", cname)
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
-    out = {"kernel": "index_score_decode", "workload": "ragged_decode_B64_L4K-128K",
+    srcs = [os.path.join(CSRC, s) for s in KERNEL_SOURCES[kernel]]
+    out = {"kernel": kernel, "workload": workload,
            "fetch_raw": f, "write_raw": w, "copy_fetch_raw": cf, "copy_write_raw": cw,
            "fetch_bytes": f * f_scale, "write_bytes": w * w_scale,
-           "bytes_per_launch": f * f_scale + w * w_scale,
-           "source_sha256": sha(INDEX_SRC)}
-    with open(TRAFFIC_FILE, "w") as fh:
+           "bytes_per_launch": f * f_scale + w * w_scale, "source_sha256": sha(srcs)}
+    with open(traffic_file(kernel), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -271,8 +442,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4, help="decode workload 1, 2, 4 or 5")
+    ap.add_argument("--config", type=int, default=4, help="headline decode workload: 1, 2, 4 or 5")
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other full-size decode batches")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -286,30 +461,43 @@ def main():
 
     import torch
 
-    import dsa_synth
     import sparse_attention_long_dsa_amd as dsa
 
     torch.cuda.set_device(0)
     dsa.lib()
-    wl = dsa_synth.workload(args.config)
-    if wl.phase != "decode":
-        sys.exit("--config must name a decode workload")
-    log(f"decode workload {wl.name}: B={wl.n_q} sum(L)={sum(wl.seq_lens)}")
-    ms, idx_ms = time_decode(wl, args.steps, args.warmup, log)
-    step_bytes, index_bytes = decode_bytes(wl)
-    tok_s = wl.n_q / (ms * 1e-3)
-    achieved = index_bytes / (idx_ms * 1e-3) / 1e9
-    traffic = traffic_for(wl.name)
+    if args.config not in (1, 2, 4, 5):
+        sys.exit("--config must name a decode workload (1, 2, 4 or 5)")
+    timer = Timer()
+    probe = None if args.no_probe else hbm_probe(log)
+    d, wl = bench_decode(args.config, timer, args.steps, args.warmup, log)
+    ms = d["ms_per_step"]
+    step_bytes, index_bytes = d["algorithmic_bytes"], d["index_algorithmic_bytes"]
+    achieved = index_bytes / (d["index_ms"] * 1e-3) / 1e9
     metric = ("decode tokens/s at 128K ctx (ragged 4K-128K, B=64, Top-K 2048)" if args.config == 4
               else f"decode tokens/s ({wl.name}, Top-K {wl.topk})")
+    roof = {"kernel": "index_score_decode (the step's dominant kernel; whole step in "
+                      "roofline_step)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for("index_score_decode", wl.name),
+            "launch_ms": d["index_ms"], "algorithmic_bytes": index_bytes}
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    roof_step = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes": step_bytes, "ms": ms}
+    if probe:
+        roof["achievable"] = probe["gbs"]
+        roof["frac_of_achievable"] = round(achieved / probe["gbs"], 4)
+        roof_step["achievable"] = probe["gbs"]
+        roof_step["frac_of_achievable"] = round(step_gbs / probe["gbs"], 4)
     res = {
         "metric": metric,
-        "value": round(tok_s, 1),
+        "value": d["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -319,31 +507,28 @@ def main():
                    "max_ctx": max(wl.seq_lens), "block_size": wl.block_size, "heads": wl.H,
                    "d_qk": wl.d_qk, "d_v": wl.d_v, "indexer": [wl.H_idx, wl.d_idx],
                    "topk": wl.topk, "seed": wl.seed},
-        "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "index_score_decode", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "launch_ms": round(idx_ms, 4),
-                     "algorithmic_bytes": index_bytes},
+        "timing": "median of event-timed steps; before each step 512 MiB written, then 512 MiB read (cache flush)",
+        "hbm_gbs_step": d["hbm_gbs_step"],
+        "hbm_frac_step": d["hbm_frac_step"],
+        "roofline": roof,
+        "roofline_step": roof_step,
+        "decode": d,
     }
+    if probe:
+        res["hbm_probe"] = probe
+    if not args.no_extra:
+        res["decode_configs"] = {}
+        for n in (2, 4, 5):
+            if n == args.config:
+                continue
+            e, ewl = bench_decode(n, timer, args.steps, args.warmup, log)
+            if probe:
+                e["hbm_frac_of_achievable"] = round(e["hbm_gbs_step"] / probe["gbs"], 4)
+            res["decode_configs"][ewl.name] = e
     if not args.no_prefill:
-        pw = dsa_synth.workload(3)
-        pms, parts, (cw_ms, cw_eager_ms, cw_bytes) = time_prefill(pw, max(2, args.steps // 4), 2, log)
-        fi, fa = prefill_flops(pw)
-        res["prefill"] = {
-            "workload": pw.name, "tokens_per_s": round(pw.seq_lens[0] / (pms * 1e-3), 1),
-            "ms_per_step": round(pms, 4), "index_ms": round(parts[0], 4),
-            "topk_ms": round(parts[1], 4), "attn_ms": round(parts[2], 4),
-            "mfma_util": round((fi + fa) / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TF, 4),
-            "attn_mfma_util": round(fa / (parts[2] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TF, 4),
-            "index_mfma_util": round(fi / (parts[0] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TF, 4),
-            "flops": fi + fa}
-        res["cache_write"] = {
-            "workload": f"{pw.name}: {pw.seq_lens[0]} tokens' latent and indexer rows",
-            "ms": round(cw_ms, 4), "ms_eager": round(cw_eager_ms, 4), "bytes": cw_bytes,
-            "gbs": round(cw_bytes / (cw_ms * 1e-3) / 1e9, 1),
-            "frac": round(cw_bytes / (cw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        p, cw = bench_prefill(timer, args.prefill_reps, 2, log)
+        res["prefill"] = p
+        res["cache_write"] = cw
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, log)
     print(json.dumps(res), flush=True)

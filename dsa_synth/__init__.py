@@ -282,6 +282,26 @@ def host_query_rows(wl: Workload, i0: int, n: int):
     return q, q_idx, w
 
 
+def host_kept_pool(wl: Workload, seq: int, positions: Sequence[int]):
+    """K/V rows of only the listed positions of one sequence, in a compact
+    pool addressed with block size 1: returns (table [1, L] int32, kv [m,
+    d_qk], v [m, d_v] or None) where table[0, p] is the pool row of a listed
+    position p (0 for the others, which must not be read).  Values are the
+    ones every other fill gives (keyed by sequence, position and column)."""
+    L = wl.seq_lens[seq]
+    keep = sorted(set(int(x) for x in positions if x >= 0))
+    table = np.zeros((1, L), dtype=np.int32)
+    table[0, keep] = np.arange(len(keep), dtype=np.int32)
+    m = max(1, len(keep))
+    kv = np.full((m, wl.d_qk), BF16_NAN, dtype=np.uint16)
+    v = np.full((m, wl.d_v), BF16_NAN, dtype=np.uint16) if wl.separate_v else None
+    for p in keep:
+        host_paged(kv, KIND_NORMAL_BF16, wl.seed, TID_KV, seq, p, 1, table[0], 1)
+        if v is not None:
+            host_paged(v, KIND_NORMAL_BF16, wl.seed, TID_V, seq, p, 1, table[0], 1)
+    return table, kv, v
+
+
 def host_sequence_pools(wl: Workload, seq: int, kv_positions: Optional[Sequence[int]] = None):
     """k_idx for every position of one sequence, plus K/V rows for only the
     positions listed (others NaN), laid out in a private pool whose block
@@ -300,6 +320,8 @@ def host_sequence_pools(wl: Workload, seq: int, kv_positions: Optional[Sequence[
     L = wl.seq_lens[seq]
     k_idx = np.full((rows, wl.d_idx), BF16_NAN, dtype=np.uint16)
     host_paged(k_idx, KIND_INT_BF16, wl.seed, TID_KIDX, seq, 0, L, lbt[0], wl.block_size, -3, 3)
+    if kv_positions is None:  # indexer keys only
+        return lbt, k_idx, None, None
     kv = np.full((rows, wl.d_qk), BF16_NAN, dtype=np.uint16)
     v = np.full((rows, wl.d_v), BF16_NAN, dtype=np.uint16) if wl.separate_v else None
     if kv_positions is not None:

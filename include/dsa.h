@@ -41,9 +41,13 @@
  *                 columns of each K row (cache->v == NULL), or (8, 64, 64)
  *                 with a separate V pool;
  *       1 <= K <= 2048; any lengths, except that one dsa_index_score
- *       prefill call takes at most 1048560 queries (chunk longer prefills);
+ *       DSA_PREFILL call takes at most 1048560 queries (chunk longer
+ *       prefills) and a DSA_DECODE call with more than 1024 queries at most
+ *       65535;
  *       block_size a multiple of 16 for dsa_index_score, any block_size >= 1
  *       for the other calls.
+ *   - Softmax scale: sm_scale may be any finite value (zero and negative
+ *     included); a non-finite scale returns DSA_ERR_SHAPE.
  *   - Precision of attention: q.K in bf16 with fp32 accumulation.  In the
  *     (128, 576, 512) family the P.V product runs in fp16 with fp32
  *     accumulation: the weights carry 11 significant bits and the values are
@@ -73,7 +77,8 @@ typedef enum {
   DSA_ERR_UNSUPPORTED = 3,  /* no kernel for this head count / width            */
   DSA_ERR_WORKSPACE = 4,    /* workspace_bytes below the matching *_workspace_size */
   DSA_ERR_DEVICE = 5,       /* current device is not gfx950 or not usable       */
-  DSA_ERR_HIP = 6           /* a HIP launch failed                              */
+  DSA_ERR_HIP = 6,          /* a HIP launch failed                              */
+  DSA_ERR_BOUNDS = 7        /* device data out of range (debug builds only)     */
 } dsa_status_t;
 
 typedef enum { DSA_PREFILL = 0, DSA_DECODE = 1 } dsa_phase_t;
@@ -99,20 +104,35 @@ typedef struct {
 } dsa_paged_cache_t;
 
 /* Index score (page 1, section 3 item (1): low-dimensional similarity
- * scoring of every past position).
+ * scoring of every past position).  Query i belongs to sequence seq_i and
+ * sits at position pos_i of it; its candidates are positions 0 .. pos_i:
  *   scores[i * ld + s] = sum_h w[i*H_idx + h] * max(0, q_idx[i,h,:] . k_idx(seq_i, s))
- * for every candidate s = 0 .. pos_i of query i; other entries of the row are
- * left unspecified.  Sums are exact for integer-valued inputs below 2^24.
- *   DSA_DECODE:  n_q == cache->n_seq; query i is the last cached token of
- *                sequence i (pos_i = seq_lens[i] - 1); prefill_seq and
- *                prefill_pos0 are ignored.  ld >= max seq_lens.
- *   DSA_PREFILL: query i is position prefill_pos0 + i of sequence
- *                prefill_seq (chunked causal prefill); ld >= prefill_pos0 + n_q.
- * q_idx: bf16 [n_q, H_idx, d_idx]; w: fp32 [n_q, H_idx]; scores: fp32 [n_q, ld]. */
+ * for s = 0 .. pos_i; other entries of the row are left unspecified.  Sums
+ * are exact for integer-valued inputs below 2^24.
+ *   q_seq, q_pos: int32 [n_q] device arrays giving seq_i and pos_i (page
+ *     "Day-0 Adaptation of Ultra-Large-Scale MoE Models on Heterogeneous AI
+ *     Accelerators", section 3.3: shapes are run-time values), with
+ *     0 <= seq_i < n_seq and 0 <= pos_i < min(ld, max_blocks_per_seq *
+ *     block_size) (device data: not checked by release builds).  Both NULL
+ *     (DSA_DECODE only): query i is the last cached token of sequence i,
+ *     pos_i = seq_lens[i] - 1, and n_q must equal cache->n_seq.
+ *   phase selects the kernel.  DSA_DECODE streams each query's indexer keys
+ *     from HBM (one query per sequence, or a few); DSA_PREFILL stages key
+ *     tiles in LDS and shares them among blocks of 16 consecutive queries,
+ *     which is fastest when consecutive queries are consecutive positions
+ *     of one sequence (a causal prefill chunk), though any mix is allowed.
+ * q_idx: bf16 [n_q, H_idx, d_idx]; w: fp32 [n_q, H_idx]; scores: fp32 [n_q, ld].
+ * DSA_PREFILL takes at most 1048560 queries per call (chunk longer prefills).
+ * workspace: dsa_index_score_ws(phase, n_q, ld) bytes (may be NULL when
+ * that is 0). */
 dsa_status_t dsa_index_score(const dsa_paged_cache_t *cache, dsa_phase_t phase,
-                             const uint16_t *q_idx, const float *w, int32_t n_q, int32_t H_idx,
-                             int32_t prefill_seq, int32_t prefill_pos0, float *scores, int64_t ld,
+                             const uint16_t *q_idx, const float *w, const int32_t *q_seq,
+                             const int32_t *q_pos, int32_t n_q, int32_t H_idx, float *scores,
+                             int64_t ld, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* Workspace bytes dsa_index_score needs (0 for every size today). */
+size_t dsa_index_score_ws(dsa_phase_t phase, int32_t n_q, int64_t ld);
 
 /* Workspace bytes dsa_topk needs for these sizes (0 is possible). */
 size_t dsa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t K);
@@ -156,14 +176,17 @@ dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t *cache, const uint16
                                     size_t workspace_bytes, hipStream_t stream);
 
 /* Sparse attention, prefill path (page 1, section 3 item (3): many queries,
- * compute bound).  Query t is position pos0 + t of sequence `seq`; same
- * formula as decode, with j over idx[t*K + r] for r < min(K, pos0 + t + 1)
- * and idx >= 0.  q: bf16 [T, H, d_qk]; out: bf16 [T, H, d_v]; lse: fp32
- * [T, H] or NULL.  No workspace. */
+ * compute bound).  Query t belongs to sequence q_seq[t] at position
+ * q_pos[t] (int32 [T] device arrays, 0 <= q_seq[t] < n_seq, 0 <= q_pos[t] <
+ * max_blocks_per_seq * block_size; queries of several sequences may share a
+ * call); same formula as decode, with j over idx[t*K + r] for
+ * r < min(K, q_pos[t] + 1) and idx >= 0.  q: bf16 [T, H, d_qk]; out: bf16
+ * [T, H, d_v]; lse: fp32 [T, H] or NULL.  No workspace. */
 dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t *cache, const uint16_t *q,
+                                     const int32_t *q_seq, const int32_t *q_pos,
                                      const int32_t *idx, int32_t T, int32_t H, int32_t K,
-                                     int32_t seq, int32_t pos0, float sm_scale, uint16_t *out,
-                                     float *lse, hipStream_t stream);
+                                     float sm_scale, uint16_t *out, float *lse,
+                                     hipStream_t stream);
 
 /* Cache write (page 1, section 3 item (2), the paged layout; page
  * "Day-0 Adaptation of Ultra-Large-Scale MoE Models on Heterogeneous AI
@@ -186,6 +209,21 @@ dsa_status_t dsa_cache_write(const dsa_paged_cache_t *cache, const int32_t *seq,
 
 /* Static text for a status code. */
 const char *dsa_status_string(dsa_status_t status);
+
+/* Checks of device data (a debug aid; page "Day-0 Adaptation of
+ * Ultra-Large-Scale MoE Models on Heterogeneous AI Accelerators", section 4:
+ * the index results decide the cache addresses, so a bad entry must be
+ * found where it is read).  In a library built with DSA_DEBUG_BOUNDS, every
+ * kernel checks the device data the host cannot see -- block-table entries
+ * (0 <= entry < num_blocks), sequence lengths and query positions against
+ * the cache description and ld, kept indices against their row's candidate
+ * count, Top-K candidate counts against ld -- replaces an out-of-range value
+ * by a safe one (block 0, nothing to score, a skipped index) and records
+ * it.  This call synchronises `stream`, then returns DSA_ERR_BOUNDS if any
+ * call since the previous check met such a value (and clears the record),
+ * else DSA_OK.  A release build checks nothing and returns
+ * DSA_ERR_UNSUPPORTED. */
+dsa_status_t dsa_check_device_errors(hipStream_t stream);
 
 #ifdef __cplusplus
 }

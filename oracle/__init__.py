@@ -21,7 +21,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsa_oracle.so")
+# DSA_ORACLE_LIB names another build of dsa_oracle.c to load instead (the
+# mutation check of the pins builds deliberately broken copies)
+LIB_PATH = os.environ.get("DSA_ORACLE_LIB") or os.path.join(_HERE, "libdsa_oracle.so")
 _lib = None
 
 

@@ -10,6 +10,8 @@ The C ABI is declared in include/dsa.h; the names here match it:
   topk               -> dsa_topk
   sparse_attn_decode -> dsa_sparse_attn_decode
   sparse_attn_prefill-> dsa_sparse_attn_prefill
+  cache_write        -> dsa_cache_write
+  check_device_errors-> dsa_check_device_errors
 """
 from __future__ import annotations
 
@@ -20,6 +22,9 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# the same sources built with DSA_DEBUG_BOUNDS: kernels check the device data
+# the host cannot see (block-table entries, lengths, positions, kept indices)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libdsa_debug.so")
 SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_latent.hip",
            "cache_write.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
@@ -28,7 +33,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
 
 DSA_PREFILL, DSA_DECODE = 0, 1
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
-          4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP"}
+          4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP", 7: "DSA_ERR_BOUNDS"}
 
 
 # Per-source extra flags.  The attention kernel keeps its MFMA accumulators
@@ -39,28 +44,53 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPP
 EXTRA_FLAGS = {"sparse_attn.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libdsa.so in-tree with hipcc for gfx950 (one object per source)."""
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile libdsa.so (or, with debug=True, libdsa_debug.so: the same
+    sources with DSA_DEBUG_BOUNDS) in-tree with hipcc for gfx950, one object
+    per source, compiled in parallel."""
     import tempfile
 
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    flags = HIPCC_FLAGS + (["-DDSA_DEBUG_BOUNDS"] if debug else [])
     with tempfile.TemporaryDirectory() as tmp:
-        objs = []
+        procs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c",
+            cmd = ["/opt/rocm/bin/hipcc", *flags, *EXTRA_FLAGS.get(src, []), "-c",
                    os.path.join(_HERE, "csrc", src), "-o", obj]
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            if r.returncode != 0:
-                raise RuntimeError(f"compiling {src} failed:\n" + r.stderr)
+            procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                     stderr=subprocess.PIPE, text=True)))
+        objs = []
+        for src, obj, p in procs:
+            _, err = p.communicate()
+            if p.returncode != 0:
+                raise RuntimeError(f"compiling {src} failed:\n" + err)
             objs.append(obj)
-        cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-shared", *objs, "-o", LIB_PATH + ".tmp"]
+        cmd = ["/opt/rocm/bin/hipcc", *flags, "-shared", *objs, "-o", path + ".tmp"]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError("linking libdsa.so failed:\n" + r.stderr)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+            raise RuntimeError(f"linking {os.path.basename(path)} failed:\n" + r.stderr)
+    os.replace(path + ".tmp", path)
     if verbose:
-        print("built", LIB_PATH)
-    return LIB_PATH
+        print("built", path)
+    return path
+
+
+PROBE_SRC = os.path.join(_HERE, "probe", "hbm_probe.hip")
+PROBE_LIB = os.path.join(_HERE, "probe", "libdsa_hbm_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the HBM streaming-read probe (a measurement aid, not part of
+    the hot path) into its own small library."""
+    cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building the HBM probe failed:\n" + r.stderr)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
 
 
 class PagedCache(ctypes.Structure):
@@ -75,6 +105,31 @@ class PagedCache(ctypes.Structure):
 
 
 _lib = None
+_debug_lib = None
+
+
+def _configure(L):
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    pc = ctypes.POINTER(PagedCache)
+    L.dsa_index_score.argtypes = [pc, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp, sz, vp]
+    L.dsa_index_score_ws.argtypes = [i32, i32, i64]
+    L.dsa_index_score_ws.restype = sz
+    L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
+    L.dsa_topk_workspace_size.restype = sz
+    L.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, sz, vp]
+    L.dsa_sparse_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.dsa_sparse_attn_decode_workspace_size.restype = sz
+    L.dsa_sparse_attn_decode.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp]
+    L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
+    L.dsa_check_device_errors.argtypes = [vp]
+    L.dsa_status_string.argtypes = [i32]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode, L.dsa_sparse_attn_prefill,
+              L.dsa_cache_write, L.dsa_check_device_errors):
+        f.restype = i32
+    return L
 
 
 def lib():
@@ -83,38 +138,31 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
-                                 ctypes.c_size_t)
-        pc = ctypes.POINTER(PagedCache)
-        L.dsa_index_score.argtypes = [pc, i32, vp, vp, i32, i32, i32, i32, vp, i64, vp]
-        L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
-        L.dsa_topk_workspace_size.restype = sz
-        L.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, sz, vp]
-        L.dsa_sparse_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
-        L.dsa_sparse_attn_decode_workspace_size.restype = sz
-        L.dsa_sparse_attn_decode.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
-        L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
-        L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
-        L.dsa_status_string.argtypes = [i32]
-        L.dsa_status_string.restype = ctypes.c_char_p
-        for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode,
-                  L.dsa_sparse_attn_prefill, L.dsa_cache_write):
-            f.restype = i32
-        _lib = L
+        _lib = _configure(ctypes.CDLL(LIB_PATH))
     return _lib
 
 
+def debug_lib():
+    """The loaded libdsa_debug.so (the DSA_DEBUG_BOUNDS build)."""
+    global _debug_lib
+    if _debug_lib is None:
+        if not os.path.exists(DEBUG_LIB_PATH):
+            raise RuntimeError(f"{DEBUG_LIB_PATH} is missing: build it with "
+                               "__graft_entry__.build()")
+        _debug_lib = _configure(ctypes.CDLL(DEBUG_LIB_PATH))
+    return _debug_lib
+
+
 class DsaError(RuntimeError):
-    def __init__(self, code: int, call: str):
-        msg = lib().dsa_status_string(code).decode()
+    def __init__(self, code: int, call: str, library=None):
+        msg = (library or lib()).dsa_status_string(code).decode()
         super().__init__(f"{call}: {STATUS.get(code, code)} ({msg})")
         self.code = code
 
 
-def _check(code: int, call: str):
+def _check(code: int, call: str, library=None):
     if code != 0:
-        raise DsaError(code, call)
+        raise DsaError(code, call, library)
 
 
 def _ptr(t) -> Optional[int]:
@@ -172,23 +220,37 @@ class Cache:
         return self.c.n_seq
 
 
-def index_score(cache: Cache, q_idx, w, phase: int, prefill_seq: int = 0, prefill_pos0: int = 0,
-                ld: Optional[int] = None, out=None, stream=None):
-    """dsa_index_score: fp32 scores [n_q, ld]."""
+def index_score(cache: Cache, q_idx, w, phase: int, q_seq=None, q_pos=None,
+                ld: Optional[int] = None, out=None, stream=None, library=None):
+    """dsa_index_score: fp32 scores [n_q, ld].  q_seq / q_pos: int32 [n_q]
+    device tensors (query i = position q_pos[i] of sequence q_seq[i]), or
+    both None in DSA_DECODE (query i = last cached token of sequence i)."""
     import torch
 
+    L = library or lib()
     _need(q_idx, torch.bfloat16, "q_idx")
     _need(w, torch.float32, "w")
+    if q_seq is not None:
+        _need(q_seq, torch.int32, "q_seq")
+    if q_pos is not None:
+        _need(q_pos, torch.int32, "q_pos")
     n_q, H_idx, _ = q_idx.shape
     if ld is None:
         ld = out.shape[1] if out is not None else None
     if out is None:
         out = torch.empty((n_q, ld), dtype=torch.float32, device=q_idx.device)
     _need(out, torch.float32, "scores")
-    _check(lib().dsa_index_score(ctypes.byref(cache.c), phase, q_idx.data_ptr(), w.data_ptr(), n_q,
-                                 H_idx, prefill_seq, prefill_pos0, out.data_ptr(), out.shape[1],
-                                 _stream(stream)), "dsa_index_score")
+    _check(L.dsa_index_score(ctypes.byref(cache.c), phase, q_idx.data_ptr(), w.data_ptr(),
+                             _ptr(q_seq), _ptr(q_pos), n_q, H_idx, out.data_ptr(), out.shape[1],
+                             None, 0, _stream(stream)), "dsa_index_score", L)
     return out
+
+
+def check_device_errors(stream=None, library=None) -> int:
+    """dsa_check_device_errors: the status (DSA_OK, DSA_ERR_BOUNDS, or
+    DSA_ERR_UNSUPPORTED in a release build)."""
+    L = library or lib()
+    return L.dsa_check_device_errors(_stream(stream))
 
 
 def topk_workspace(n_q: int, ld: int, K: int, device="cuda"):
@@ -199,10 +261,11 @@ def topk_workspace(n_q: int, ld: int, K: int, device="cuda"):
 
 
 def topk(scores, K: int, n_valid=None, causal_base: int = 0, out=None, workspace=None,
-         stream=None):
+         stream=None, library=None):
     """dsa_topk: int32 [n_q, K] ascending kept positions, -1 padded."""
     import torch
 
+    L = library or lib()
     _need(scores, torch.float32, "scores")
     n_q, ld = scores.shape
     if n_valid is not None:
@@ -212,9 +275,9 @@ def topk(scores, K: int, n_valid=None, causal_base: int = 0, out=None, workspace
     _need(out, torch.int32, "idx")
     if workspace is None:
         workspace = topk_workspace(n_q, ld, K, scores.device)
-    _check(lib().dsa_topk(scores.data_ptr(), ld, n_q, K, _ptr(n_valid), causal_base,
-                          out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                          _stream(stream)), "dsa_topk")
+    _check(L.dsa_topk(scores.data_ptr(), ld, n_q, K, _ptr(n_valid), causal_base,
+                      out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "dsa_topk", L)
     return out
 
 
@@ -226,10 +289,11 @@ def decode_workspace(B: int, H: int, K: int, d_v: int, device="cuda"):
 
 
 def sparse_attn_decode(cache: Cache, q, idx, sm_scale: float, out=None, lse=None,
-                       workspace=None, want_lse: bool = True, stream=None):
+                       workspace=None, want_lse: bool = True, stream=None, library=None):
     """dsa_sparse_attn_decode: (bf16 out [B, H, d_v], fp32 lse [B, H])."""
     import torch
 
+    L = library or lib()
     _need(q, torch.bfloat16, "q")
     _need(idx, torch.int32, "idx")
     B, H, _ = q.shape
@@ -241,20 +305,25 @@ def sparse_attn_decode(cache: Cache, q, idx, sm_scale: float, out=None, lse=None
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = decode_workspace(B, H, K, d_v, q.device)
-    _check(lib().dsa_sparse_attn_decode(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), B, H,
-                                        K, float(sm_scale), out.data_ptr(), _ptr(lse),
-                                        workspace.data_ptr(), workspace.numel(), _stream(stream)),
-           "dsa_sparse_attn_decode")
+    _check(L.dsa_sparse_attn_decode(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), B, H,
+                                    K, float(sm_scale), out.data_ptr(), _ptr(lse),
+                                    workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "dsa_sparse_attn_decode", L)
     return out, lse
 
 
-def sparse_attn_prefill(cache: Cache, q, idx, seq: int, pos0: int, sm_scale: float, out=None,
-                        lse=None, want_lse: bool = True, stream=None):
-    """dsa_sparse_attn_prefill: (bf16 out [T, H, d_v], fp32 lse [T, H])."""
+def sparse_attn_prefill(cache: Cache, q, q_seq, q_pos, idx, sm_scale: float, out=None,
+                        lse=None, want_lse: bool = True, stream=None, library=None):
+    """dsa_sparse_attn_prefill: (bf16 out [T, H, d_v], fp32 lse [T, H]).
+    q_seq, q_pos: int32 [T] device tensors (query t = position q_pos[t] of
+    sequence q_seq[t])."""
     import torch
 
+    L = library or lib()
     _need(q, torch.bfloat16, "q")
     _need(idx, torch.int32, "idx")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(q_pos, torch.int32, "q_pos")
     T, H, _ = q.shape
     K = idx.shape[1]
     d_v = cache.c.d_v
@@ -262,13 +331,15 @@ def sparse_attn_prefill(cache: Cache, q, idx, seq: int, pos0: int, sm_scale: flo
         out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    _check(lib().dsa_sparse_attn_prefill(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), T, H,
-                                         K, seq, pos0, float(sm_scale), out.data_ptr(), _ptr(lse),
-                                         _stream(stream)), "dsa_sparse_attn_prefill")
+    _check(L.dsa_sparse_attn_prefill(ctypes.byref(cache.c), q.data_ptr(), q_seq.data_ptr(),
+                                     q_pos.data_ptr(), idx.data_ptr(), T, H, K, float(sm_scale),
+                                     out.data_ptr(), _ptr(lse), _stream(stream)),
+           "dsa_sparse_attn_prefill", L)
     return out, lse
 
 
-def cache_write(cache: Cache, seq, pos, kv_new, k_idx_new, v_new=None, stream=None):
+def cache_write(cache: Cache, seq, pos, kv_new, k_idx_new, v_new=None, stream=None,
+                library=None):
     """dsa_cache_write: store new tokens' rows into the paged pools in place.
 
     seq, pos: int32 [n]; kv_new: bf16 [n, d_qk]; k_idx_new: bf16 [n, d_idx];
@@ -282,9 +353,10 @@ def cache_write(cache: Cache, seq, pos, kv_new, k_idx_new, v_new=None, stream=No
     if v_new is not None:
         _need(v_new, torch.bfloat16, "v_new")
     n = seq.shape[0]
-    _check(lib().dsa_cache_write(ctypes.byref(cache.c), seq.data_ptr(), pos.data_ptr(), n,
-                                 kv_new.data_ptr(), _ptr(v_new), k_idx_new.data_ptr(),
-                                 _stream(stream)), "dsa_cache_write")
+    L = library or lib()
+    _check(L.dsa_cache_write(ctypes.byref(cache.c), seq.data_ptr(), pos.data_ptr(), n,
+                             kv_new.data_ptr(), _ptr(v_new), k_idx_new.data_ptr(),
+                             _stream(stream)), "dsa_cache_write", L)
 
 
 class DecodeStep:
@@ -304,37 +376,43 @@ class DecodeStep:
         self.ws_topk = topk_workspace(B, ld, K, device)
         self.ws_attn = decode_workspace(B, H, K, d_v, device)
 
-    def __call__(self, q, q_idx, w, sm_scale: float, stream=None):
+    def __call__(self, q, q_idx, w, sm_scale: float, stream=None, library=None):
         c = self.cache
-        index_score(c, q_idx, w, DSA_DECODE, out=self.scores, stream=stream)
+        index_score(c, q_idx, w, DSA_DECODE, out=self.scores, stream=stream, library=library)
         topk(self.scores, self.K, n_valid=c.tensors[3], out=self.idx, workspace=self.ws_topk,
-             stream=stream)
+             stream=stream, library=library)
         sparse_attn_decode(c, q, self.idx, sm_scale, out=self.out, lse=self.lse,
-                           workspace=self.ws_attn, stream=stream)
+                           workspace=self.ws_attn, stream=stream, library=library)
         return self.out, self.lse
 
 
 class PrefillStep:
-    """Causal prefill of positions pos0 .. pos0+T-1 of one sequence."""
+    """Causal prefill of positions pos0 .. pos0+T-1 of sequence `seq` (or, with
+    q_seq / q_pos given, of any queries: q_seq[t], q_pos[t])."""
 
     def __init__(self, cache: Cache, T: int, H: int, K: int, d_v: int, pos0: int = 0,
-                 device="cuda"):
+                 seq: int = 0, q_seq=None, q_pos=None, device="cuda"):
         import torch
 
-        self.cache, self.K, self.T, self.pos0 = cache, K, T, pos0
-        ld = (pos0 + T + 63) // 64 * 64  # aligned score rows
+        self.cache, self.K, self.T = cache, K, T
+        if q_pos is None:
+            q_pos = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=device)
+            q_seq = torch.full((T,), seq, dtype=torch.int32, device=device)
+        self.q_seq, self.q_pos = q_seq, q_pos
+        self.n_valid = q_pos + 1  # candidates of each row: positions 0 .. q_pos
+        ld = (int(q_pos.max().item()) + 1 + 63) // 64 * 64  # aligned score rows
         self.scores = torch.empty((T, ld), dtype=torch.float32, device=device)
         self.idx = torch.empty((T, K), dtype=torch.int32, device=device)
         self.out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
         self.ws_topk = topk_workspace(T, ld, K, device)
 
-    def __call__(self, q, q_idx, w, sm_scale: float, seq: int = 0, stream=None):
+    def __call__(self, q, q_idx, w, sm_scale: float, stream=None, library=None):
         c = self.cache
-        index_score(c, q_idx, w, DSA_PREFILL, prefill_seq=seq, prefill_pos0=self.pos0,
-                    out=self.scores, stream=stream)
-        topk(self.scores, self.K, causal_base=self.pos0, out=self.idx, workspace=self.ws_topk,
-             stream=stream)
-        sparse_attn_prefill(c, q, self.idx, seq, self.pos0, sm_scale, out=self.out, lse=self.lse,
-                            stream=stream)
+        index_score(c, q_idx, w, DSA_PREFILL, q_seq=self.q_seq, q_pos=self.q_pos,
+                    out=self.scores, stream=stream, library=library)
+        topk(self.scores, self.K, n_valid=self.n_valid, out=self.idx, workspace=self.ws_topk,
+             stream=stream, library=library)
+        sparse_attn_prefill(c, q, self.q_seq, self.q_pos, self.idx, sm_scale, out=self.out,
+                            lse=self.lse, stream=stream, library=library)
         return self.out, self.lse

@@ -15,6 +15,44 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// The queries of an attention call.  Decode: query i is the last cached
+// token of sequence i (seq_lens[i] candidates).  Prefill: query i belongs to
+// sequence q_seq[i] at position q_pos[i] (q_pos[i] + 1 candidates).  Debug
+// builds check both against the cache description and give a query outside
+// it no candidates.
+struct AttnQuery {
+  const int32_t* seq_lens;  // decode, else NULL
+  const int32_t* q_seq;     // prefill, else NULL
+  const int32_t* q_pos;     // prefill, else NULL
+  int n_seq, max_pos, num_blocks;
+  __device__ __forceinline__ bool decode() const { return seq_lens != nullptr; }
+  __device__ __forceinline__ int seq(int i) const {
+    const int b = q_seq ? q_seq[i] : i;
+    if (kCheckBounds && (b < 0 || b >= n_seq)) return 0;
+    return b;
+  }
+  __device__ __forceinline__ int count(int i) const {
+    const int n = q_pos ? q_pos[i] + 1 : seq_lens[i];
+    if (kCheckBounds) {
+      const int b = q_seq ? q_seq[i] : i;
+      if (b < 0 || b >= n_seq || n < 0 || n > max_pos) {
+        raise_error(q_pos ? kErrQuery : kErrLength);
+        return 0;
+      }
+    }
+    return n;
+  }
+  // A kept index of a row with n candidates (debug builds: one at or past n
+  // is skipped).
+  __device__ __forceinline__ int kept(int pos, int n) const {
+    if (kCheckBounds && pos >= n) {
+      raise_error(kErrIndex);
+      return -1;
+    }
+    return pos;
+  }
+};
+
 // Split-K plan for decode: enough workgroups to cover the chip about twice.
 struct SplitPlan {
   int n_splits, tiles_per_split;
@@ -127,9 +165,12 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const PT* __restrict_
 
 // Launches the latent-row kernel (128 heads on a 576-wide row, V = its
 // first 512 columns), and the split merge when plan.n_splits > 1.
-__attribute__((visibility("hidden"))) void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
-                   int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
-                   uint16_t* out, float* lse, uint16_t* part_o, float* part_lse, SplitPlan plan,
-                   hipStream_t stream);
+__attribute__((visibility("hidden"))) void launch_latent(const dsa_paged_cache_t* c,
+                                                        const uint16_t* q, const int32_t* idx,
+                                                        int n_q, int K, AttnQuery aq,
+                                                        float sm_scale, uint16_t* out, float* lse,
+                                                        uint16_t* part_o, float* part_lse,
+                                                        SplitPlan plan, hipStream_t stream);
+__attribute__((visibility("hidden"))) uint32_t take_bounds_error_latent(hipStream_t stream);
 
 }  // namespace dsa

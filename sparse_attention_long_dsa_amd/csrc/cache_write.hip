@@ -46,6 +46,11 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(
 }
 
 }  // namespace
+
+// Tokens outside the cache description are skipped by contract, so the
+// cache write raises no debug error; its word stays 0.
+uint32_t take_bounds_error_cache_write(hipStream_t stream) { return take_bounds_error(stream); }
+
 }  // namespace dsa
 
 extern "C" dsa_status_t dsa_cache_write(const dsa_paged_cache_t* cache, const int32_t* seq,

@@ -83,10 +83,68 @@ __device__ __forceinline__ void global_to_lds16(const void* src, uint32_t lds) {
       : "v"(src), "s"(lds)
       : "memory");
 }
+// Checks of device data in debug builds (compiled with DSA_DEBUG_BOUNDS).
+// The host never reads block-table entries, lengths, query positions or kept
+// indices (that would need a synchronisation); a debug build checks each of
+// them where a kernel reads it, replaces an out-of-range value by a safe one
+// (block 0, nothing to score, a skipped index) and raises a bit of the
+// translation unit's error word, which dsa_check_device_errors reads and
+// clears.  Release builds compile the checks away.
+#ifdef DSA_DEBUG_BOUNDS
+constexpr bool kCheckBounds = true;
+#else
+constexpr bool kCheckBounds = false;
+#endif
+enum : uint32_t {
+  kErrBlock = 1u,     // a block-table entry outside [0, num_blocks)
+  kErrQuery = 2u,     // a query's sequence or position outside the cache description
+  kErrIndex = 4u,     // a kept index at or past its row's candidate count
+  kErrLength = 8u,    // a sequence length or candidate count out of range
+};
+
+namespace {
+#ifdef DSA_DEBUG_BOUNDS
+__device__ uint32_t g_bounds_error;  // one per translation unit
+#endif
+__device__ __forceinline__ void raise_error(uint32_t bits) {
+#ifdef DSA_DEBUG_BOUNDS
+  atomicOr(&g_bounds_error, bits);
+#else
+  (void)bits;
+#endif
+}
+// Reads and clears this translation unit's error word (0 in release builds).
+inline uint32_t take_bounds_error(hipStream_t stream) {
+#ifdef DSA_DEBUG_BOUNDS
+  uint32_t v = 0, zero = 0;
+  if (hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_bounds_error), 4, 0, hipMemcpyDeviceToHost,
+                               stream) != hipSuccess ||
+      hipMemcpyToSymbolAsync(HIP_SYMBOL(g_bounds_error), &zero, 4, 0, hipMemcpyHostToDevice,
+                             stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return 0x80000000u;
+  return v;
+#else
+  (void)stream;
+  return 0;
+#endif
+}
+}  // namespace
+
+// A block-table entry, checked in debug builds.
+__device__ __forceinline__ int32_t checked_block(int32_t blk, int num_blocks) {
+  if (kCheckBounds && (uint32_t)blk >= (uint32_t)num_blocks) {
+    raise_error(kErrBlock);
+    return 0;
+  }
+  return blk;
+}
+
 // Physical pool row of logical position `pos` of the sequence whose block
 // table row is `bt_row`.
-__device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt_row, int bs, int pos) {
-  return (int64_t)bt_row[pos / bs] * bs + pos % bs;
+__device__ __forceinline__ int64_t paged_row(const int32_t* __restrict__ bt_row, int bs, int pos,
+                                             int num_blocks) {
+  return (int64_t)checked_block(bt_row[pos / bs], num_blocks) * bs + pos % bs;
 }
 
 // The gfx950 row swaps: after permlane16_swap(x, x) the first register holds

@@ -39,4 +39,10 @@ inline dsa_status_t check_cache_common(const dsa_paged_cache_t* c) {
   return DSA_OK;
 }
 
+// Each translation unit's debug error word, read and cleared (0 in release
+// builds; bit 31 set when reading failed).
+__attribute__((visibility("hidden"))) uint32_t take_bounds_error_index_score(hipStream_t stream);
+__attribute__((visibility("hidden"))) uint32_t take_bounds_error_topk(hipStream_t stream);
+__attribute__((visibility("hidden"))) uint32_t take_bounds_error_cache_write(hipStream_t stream);
+
 }  // namespace dsa

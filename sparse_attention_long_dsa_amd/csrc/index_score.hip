@@ -39,7 +39,7 @@ constexpr int kWaves = kThreads / kWave;
 template <int H_IDX, int D_IDX, int UNROLL>
 __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx, int64_t k_stride,
                                               const int32_t* __restrict__ bt_row, int bs,
-                                              const uint16_t* __restrict__ q_row,
+                                              int num_blocks, const uint16_t* __restrict__ q_row,
                                               const float* __restrict__ w_row,
                                               float* __restrict__ out, int t0, int t1) {
   constexpr int HT = (H_IDX + 15) / 16;  // 16-head tiles
@@ -85,7 +85,7 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int g0 = __builtin_amdgcn_readfirstlane(min(base + 16 * u, g_last));
-      const int64_t phys = bt_row[g0 / bs];
+      const int64_t phys = checked_block(bt_row[g0 / bs], num_blocks);
       const uint16_t* row = k_idx + (phys * bs + g0 % bs + col) * k_stride + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kb[u][ks] = *(const u32x4*)(row + 32 * ks);
@@ -131,6 +131,30 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
 constexpr int kUnroll = 4;      // 16-position groups per wave per register buffer
 constexpr int kFlatMaxSeq = 1024;
 
+// Query i of a call: its sequence and its candidate count (positions
+// 0 .. n - 1).  Without per-query arrays, query i is the last cached token
+// of sequence i.  Debug builds check the description against the cache and
+// score nothing for a query outside it.
+struct QueryDesc {
+  const int32_t* q_seq;     // [n_q] or NULL
+  const int32_t* q_pos;     // [n_q] or NULL
+  const int32_t* seq_lens;  // [n_seq], used when q_pos is NULL
+  int n_seq, max_pos;       // max_pos = max_blocks_per_seq * block_size
+  int64_t ld;
+  __device__ __forceinline__ int seq(int i) const { return q_seq ? q_seq[i] : i; }
+  __device__ __forceinline__ int count(int i) const {
+    const int n = q_pos ? q_pos[i] + 1 : seq_lens[i];
+    if (kCheckBounds) {
+      const int b = seq(i);
+      if (b < 0 || b >= n_seq || n < 0 || n > max_pos || n > ld) {
+        raise_error(q_pos ? kErrQuery : kErrLength);
+        return 0;
+      }
+    }
+    return n;
+  }
+};
+
 // Decode, token-balanced: the batch's positions are laid end to end and
 // each workgroup of a persistent grid takes one equal slice, whatever the
 // ragged lengths; the query is reloaded only where a slice crosses into the
@@ -138,7 +162,7 @@ constexpr int kFlatMaxSeq = 1024;
 template <int H_IDX, int D_IDX>
 __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
-    int max_blocks, int bs, const int32_t* __restrict__ seq_lens, int n_seq,
+    int max_blocks, int bs, int num_blocks, QueryDesc qd, int n_seq,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     float* __restrict__ scores, int64_t ld) {
   __shared__ int64_t cum[kFlatMaxSeq + 1];
@@ -148,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
   const int per = (n_seq + kThreads - 1) / kThreads;
   const int s0 = threadIdx.x * per, s1 = min(s0 + per, n_seq);
   int64_t run = 0;
-  for (int i = s0; i < s1; ++i) run += seq_lens[i];
+  for (int i = s0; i < s1; ++i) run += qd.count(i);
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int64_t incl = run;
 #pragma unroll
@@ -167,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
   run = base + incl - run;  // exclusive prefix of this thread's run
   for (int i = s0; i < s1; ++i) {
     cum[i] = run;
-    run += seq_lens[i];
+    run += qd.count(i);
   }
   if (threadIdx.x == 0) cum[n_seq] = total_all;
   __syncthreads();
@@ -185,9 +209,10 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     const int t0 = (int)max<int64_t>(lo - cum[b], 0);
     const int t1 = (int)min<int64_t>(hi - cum[b], cum[b + 1] - cum[b]);
     if (t0 >= t1) continue;
-    score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride, block_table + (int64_t)b * max_blocks,
-                                         bs, q_idx + (int64_t)b * H_IDX * D_IDX,
-                                         w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0, t1);
+    score_segment<H_IDX, D_IDX, kUnroll>(
+        k_idx, k_stride, block_table + (int64_t)qd.seq(b) * max_blocks, bs, num_blocks,
+        q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0,
+        t1);
   }
 }
 
@@ -196,92 +221,145 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
 template <int H_IDX, int D_IDX>
 __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
-    int max_blocks, int bs, const int32_t* __restrict__ seq_lens,
+    int max_blocks, int bs, int num_blocks, QueryDesc qd,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     float* __restrict__ scores, int64_t ld, int chunk) {
   const int b = blockIdx.y;
-  const int L = seq_lens[b];
+  const int L = qd.count(b);
   const int t0 = blockIdx.x * chunk;
   if (t0 >= L) return;
-  score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride, block_table + (int64_t)b * max_blocks, bs,
-                                       q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX,
-                                       scores + (int64_t)b * ld, t0, min(t0 + chunk, L));
+  score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride,
+                                       block_table + (int64_t)qd.seq(b) * max_blocks, bs,
+                                       num_blocks, q_idx + (int64_t)b * H_IDX * D_IDX,
+                                       w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0,
+                                       min(t0 + chunk, L));
 }
 
 // ---------------------------------------------------------------- prefill
+//
+// Prefill queries come in blocks of consecutive queries that usually belong
+// to one sequence (a causal prefill chunk).  A block whose queries span
+// several sequences is handled one sequence at a time: the block stages that
+// sequence's keys and only its queries score them.
+
+// The sequences and positions of a block's queries, staged in LDS; `lead[g]`
+// is true when query g is the first of the block with its sequence.
+template <int QB>
+struct BlockQueries {
+  int32_t seq[QB], pos[QB];
+  __device__ void stage(const QueryDesc& qd, int q0, int qend) {
+    for (int g = threadIdx.x; g < QB; g += blockDim.x) {
+      const int qi = q0 + g;
+      int b = -1, p = -1;
+      if (qi < qend) {
+        b = qd.seq(qi);
+        p = qd.count(qi) - 1;  // -1: nothing to score (count 0)
+        if (p < 0) b = -1;
+      }
+      seq[g] = b;
+      pos[g] = p;
+    }
+  }
+  // Is query g the first of the block with its sequence?
+  __device__ bool lead(int g) const {
+    if (seq[g] < 0) return false;
+    for (int h = 0; h < g; ++h)
+      if (seq[h] == seq[g]) return false;
+    return true;
+  }
+  // Largest position among the block's queries of sequence b.
+  __device__ int last_pos(int b) const {
+    int m = -1;
+    for (int h = 0; h < QB; ++h)
+      if (seq[h] == b) m = max(m, pos[h]);
+    return m;
+  }
+};
 
 template <int H_IDX, int D_IDX, int QB, int KB>
 __global__ __launch_bounds__(kThreads) void index_score_prefill_tile_kernel(
-    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ bt_row,
-    int bs, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int n_q, int pos0,
-    float* __restrict__ scores, int64_t ld) {
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, int num_blocks, QueryDesc qd, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, int n_q, float* __restrict__ scores, int64_t ld) {
   constexpr int HT = (H_IDX + 15) / 16;
   constexpr int KS = D_IDX / 32;
   constexpr int ROW = D_IDX + 8;  // padded LDS row (elements)
   constexpr int CH = D_IDX / 8;   // 16-byte chunks per key row
   __shared__ __attribute__((aligned(16))) uint16_t ktile[KB * ROW];
+  __shared__ BlockQueries<QB> bq;
 
   const int q0 = blockIdx.y * QB;
   const int qend = min(q0 + QB, n_q);
   const int k0 = blockIdx.x * KB;
-  const int last_pos = pos0 + qend - 1;  // largest query position of the block
-  if (k0 > last_pos) return;
-  const int kend = min(k0 + KB, last_pos + 1);
-
-  for (int c = threadIdx.x; c < KB * CH; c += kThreads) {
-    const int r = c / CH, ch = c % CH;
-    const int pos = k0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (pos < kend) v = *(const u32x4*)(k_idx + paged_row(bt_row, bs, pos) * k_stride + 8 * ch);
-    *(u32x4*)(ktile + r * ROW + 8 * ch) = v;
-  }
+  bq.stage(qd, q0, qend);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int col = lane & 15, grp = lane >> 4;
-  for (int qi = q0 + wave; qi < qend; qi += kWaves) {
-    const int n = min(kend, pos0 + qi + 1) - k0;  // keys of this tile the query sees
-    if (n <= 0) continue;
-    bf16x8 qa[HT][KS];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int head = 16 * ht + col;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (head < H_IDX)
-          v = *(const u32x4*)(q_idx + ((int64_t)qi * H_IDX + head) * D_IDX + 32 * ks + 8 * grp);
-        qa[ht][ks] = as_bf16x8(v);
-      }
+  for (int lg = 0; lg < QB; ++lg) {
+    if (!bq.lead(lg)) continue;  // uniform: LDS data
+    const int b = bq.seq[lg];
+    const int last_pos = bq.last_pos(b);
+    if (k0 > last_pos) continue;
+    const int kend = min(k0 + KB, last_pos + 1);
+    const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
+    __syncthreads();  // the previous sequence's tile is no longer read
+    for (int c = threadIdx.x; c < KB * CH; c += kThreads) {
+      const int r = c / CH, ch = c % CH;
+      const int pos = k0 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (pos < kend)
+        v = *(const u32x4*)(k_idx + paged_row(bt_row, bs, pos, num_blocks) * k_stride + 8 * ch);
+      *(u32x4*)(ktile + r * ROW + 8 * ch) = v;
     }
-    float wr[HT][4];
+    __syncthreads();
+
+    for (int g = wave; g < qend - q0; g += kWaves) {
+      if (bq.seq[g] != b) continue;
+      const int qi = q0 + g;
+      const int n = min(kend, bq.pos[g] + 1) - k0;  // keys of this tile the query sees
+      if (n <= 0) continue;
+      bf16x8 qa[HT][KS];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+      for (int ht = 0; ht < HT; ++ht) {
+        const int head = 16 * ht + col;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int head = 16 * ht + 4 * grp + i;
-        wr[ht][i] = head < H_IDX ? w[(int64_t)qi * H_IDX + head] : 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (head < H_IDX)
+            v = *(const u32x4*)(q_idx + ((int64_t)qi * H_IDX + head) * D_IDX + 32 * ks + 8 * grp);
+          qa[ht][ks] = as_bf16x8(v);
+        }
       }
-    float* out = scores + (int64_t)qi * ld + k0;
-    for (int g = 0; g * 16 < n; ++g) {
-      f32x4 acc[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kb =
-            as_bf16x8(*(const u32x4*)(ktile + (16 * g + col) * ROW + 32 * ks + 8 * grp));
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
-      }
-      float s = 0.f;
+      float wr[HT][4];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += wr[ht][i] * relu(acc[ht][i]);
-      s = wave_sum_xor_16_32(s);
-      if (grp == 0 && 16 * g + col < n) out[16 * g + col] = s;
+        for (int i = 0; i < 4; ++i) {
+          const int head = 16 * ht + 4 * grp + i;
+          wr[ht][i] = head < H_IDX ? w[(int64_t)qi * H_IDX + head] : 0.f;
+        }
+      float* out = scores + (int64_t)qi * ld + k0;
+      for (int gg = 0; gg * 16 < n; ++gg) {
+        f32x4 acc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kb =
+              as_bf16x8(*(const u32x4*)(ktile + (16 * gg + col) * ROW + 32 * ks + 8 * grp));
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s += wr[ht][i] * relu(acc[ht][i]);
+        s = wave_sum_xor_16_32(s);
+        if (grp == 0 && 16 * gg + col < n) out[16 * gg + col] = s;
+      }
     }
   }
 }
@@ -293,13 +371,13 @@ __global__ __launch_bounds__(kThreads) void index_score_prefill_tile_kernel(
 // tile, and every key tile staged in LDS serves 16 queries; key tiles go
 // from HBM straight into LDS (direct loads, one tile ahead, no registers).
 // Four waves per SIMD hide the LDS latency and overlap one wave's
-// ReLU-weight-sum epilogue with another's products.  A tile row's sixteen 16-byte chunks are XOR-swizzled
-// by the row index, so the 16 lanes that read 16 rows at one chunk hit 16
-// different bank groups; the direct loads honour the same map.
+// ReLU-weight-sum epilogue with another's products.  A tile row's sixteen
+// 16-byte chunks are XOR-swizzled by the row index, so the 16 lanes that
+// read 16 rows at one chunk hit 16 different bank groups; the direct loads
+// honour the same map.
 namespace pf {
 constexpr int kWaves = 16, kThreads = kWaves * kWave;
-constexpr int kQW = 1;                                // queries per wave
-constexpr int kQB = kWaves * kQW;                     // queries per workgroup
+constexpr int kQB = kWaves;                           // queries per workgroup (one per wave)
 constexpr int kKT = 128;                              // keys per tile
 constexpr int kChunk = 64;                            // tiles per workgroup at most (8192 keys)
 constexpr int kD = 128;
@@ -310,115 +388,107 @@ constexpr int kLoads = kTileBytes / (16 * kThreads);  // wave loads per wave per
 
 template <int H_IDX>
 __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
-    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ bt_row,
-    int bs, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int n_q, int pos0,
-    float* __restrict__ scores, int64_t ld) {
-  using pf::kChunk, pf::kD, pf::kKT, pf::kLoads, pf::kQB, pf::kQW, pf::kRowChunks,
-      pf::kTileBytes;
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, int num_blocks, QueryDesc qd, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, int n_q, float* __restrict__ scores, int64_t ld) {
+  using pf::kChunk, pf::kD, pf::kKT, pf::kLoads, pf::kQB, pf::kRowChunks, pf::kTileBytes;
   constexpr int HT = H_IDX / 16, KS = kD / 32;
   __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
   __shared__ int32_t prow[kChunk * kKT];
+  __shared__ BlockQueries<kQB> bq;
 
-  // the longest query blocks (latest positions) first, so that the short ones
-  // fill in behind them
+  // the query blocks of the latest positions (usually the longest rows)
+  // first, so that the short ones fill in behind them
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kQB;
   const int qend = min(q0 + kQB, n_q);
-  const int last_pos = pos0 + qend - 1;  // largest query position of the workgroup
   const int k_begin = blockIdx.x * (kChunk * kKT);
-  if (k_begin > last_pos) return;
-  const int k_end = min(k_begin + kChunk * kKT, last_pos + 1);
-  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
-
-  // physical rows of the chunk's keys; slots past k_end repeat the first
-  // key (finite data, never stored)
-  for (int r = threadIdx.x; r < n_tiles * kKT; r += pf::kThreads) {
-    const int pos = k_begin + r;
-    prow[r] = (int32_t)paged_row(bt_row, bs, pos < k_end ? pos : k_begin);
-  }
+  bq.stage(qd, q0, qend);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15, grp = lane >> 4;
 
-  // this wave's queries: q as the A operand (head 16 ht + col, dims
+  // this wave's query: q as the A operand (head 16 ht + col, dims
   // 32 ks + 8 grp ..), the weights of the heads in this lane's result rows
-  bf16x8 qa[kQW][HT][KS];
-  float wr[kQW][HT][4];
-  int qpos[kQW];
+  const int qi = q0 + wave;
+  const int qr = qi < qend ? qi : q0;
+  bf16x8 qa[HT][KS];
+  float wr[HT][4];
 #pragma unroll
-  for (int qq = 0; qq < kQW; ++qq) {
-    const int qi = q0 + kQW * wave + qq;
-    const bool ok = qi < qend;
-    qpos[qq] = ok ? pos0 + qi : -1;
-    const int qr = ok ? qi : q0;
+  for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
+    for (int ks = 0; ks < KS; ++ks)
+      qa[ht][ks] = as_bf16x8(
+          *(const u32x4*)(q_idx + ((int64_t)qr * H_IDX + 16 * ht + col) * kD + 32 * ks + 8 * grp));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qa[qq][ht][ks] = as_bf16x8(
-            *(const u32x4*)(q_idx + ((int64_t)qr * H_IDX + 16 * ht + col) * kD + 32 * ks + 8 * grp));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[qq][ht][i] = w[(int64_t)qr * H_IDX + 16 * ht + 4 * grp + i];
-    }
+    for (int i = 0; i < 4; ++i) wr[ht][i] = w[(int64_t)qr * H_IDX + 16 * ht + 4 * grp + i];
   }
-  __syncthreads();  // prow
+  __syncthreads();  // bq
 
-  // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
-  // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ktile;
   const uint64_t row_bytes = (uint64_t)k_stride * 2;
-  auto load_tile = [&](int j, int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int blk = kLoads * wave + i;
-      const int slot = kWave * blk + lane;
-      const int r = slot / kRowChunks;
-      const int c = (slot % kRowChunks) ^ (r % kRowChunks);
-      const char* src = (const char*)k_idx + (uint64_t)(uint32_t)prow[j * kKT + r] * row_bytes + 16 * c;
-      global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * blk));
-    }
-  };
-  load_tile(0, 0);
+  for (int lg = 0; lg < kQB; ++lg) {
+    if (!bq.lead(lg)) continue;  // uniform: LDS data
+    const int b = bq.seq[lg];
+    const int last_pos = bq.last_pos(b);
+    if (k_begin > last_pos) continue;
+    const int k_end = min(k_begin + kChunk * kKT, last_pos + 1);
+    const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
+    const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
+    // this wave's query position if it belongs to sequence b (wave-uniform)
+    const int qpos = qi < qend && bq.seq[wave] == b ? bq.pos[wave] : -1;
 
-  for (int j = 0; j < n_tiles; ++j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
-    __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
-    if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
-    const uint16_t* kt = ktile[j & 1];
-    const int k0 = k_begin + j * kKT;
-    int n[kQW], n_max = 0;  // keys of this tile each query sees (wave-uniform)
-#pragma unroll
-    for (int qq = 0; qq < kQW; ++qq) {
-      n[qq] = min(kKT, max(0, qpos[qq] + 1 - k0));
-      n_max = max(n_max, n[qq]);
+    __syncthreads();  // the previous sequence's tiles and rows are no longer read
+    // physical rows of the chunk's keys; slots past k_end repeat the first
+    // key (finite data, never stored)
+    for (int r = threadIdx.x; r < n_tiles * kKT; r += pf::kThreads) {
+      const int pos = k_begin + r;
+      prow[r] = (int32_t)paged_row(bt_row, bs, pos < k_end ? pos : k_begin, num_blocks);
     }
-    for (int g = 0; 16 * g < n_max; ++g) {
-      f32x4 acc[kQW][HT];
+    __syncthreads();  // prow
+
+    // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
+    // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.
+    auto load_tile = [&](int j, int buf) {
 #pragma unroll
-      for (int qq = 0; qq < kQW; ++qq)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
-        const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
-#pragma unroll
-        for (int qq = 0; qq < kQW; ++qq)
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = mfma16x16x32(qa[qq][ht][ks], kb, acc[qq][ht]);
+      for (int i = 0; i < kLoads; ++i) {
+        const int blk = kLoads * wave + i;
+        const int slot = kWave * blk + lane;
+        const int r = slot / kRowChunks;
+        const int c = (slot % kRowChunks) ^ (r % kRowChunks);
+        const char* src =
+            (const char*)k_idx + (uint64_t)(uint32_t)prow[j * kKT + r] * row_bytes + 16 * c;
+        global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * blk));
       }
+    };
+    load_tile(0, 0);
+
+    for (int j = 0; j < n_tiles; ++j) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
+      __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
+      if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
+      const uint16_t* kt = ktile[j & 1];
+      const int k0 = k_begin + j * kKT;
+      const int n = min(kKT, max(0, qpos + 1 - k0));  // keys of this tile the query sees
+      for (int g = 0; 16 * g < n; ++g) {
+        f32x4 acc[HT];
 #pragma unroll
-      for (int qq = 0; qq < kQW; ++qq) {
-        if (16 * g >= n[qq]) continue;
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
+          const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
+        }
         float sc = 0.f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc += wr[qq][ht][i] * relu(acc[qq][ht][i]);
+          for (int i = 0; i < 4; ++i) sc += wr[ht][i] * relu(acc[ht][i]);
         sc = wave_sum_xor_16_32(sc);
-        if (grp == 0 && r < n[qq])
-          scores[(int64_t)(qpos[qq] - pos0) * ld + k0 + r] = sc;
+        if (grp == 0 && r < n) scores[(int64_t)qi * ld + k0 + r] = sc;
       }
     }
   }
@@ -426,8 +496,13 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
 
 template <int H_IDX, int D_IDX>
 dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
-                                const uint16_t* q_idx, const float* w, int n_q, int seq, int pos0,
-                                float* scores, int64_t ld, hipStream_t stream) {
+                                const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                const int32_t* q_pos, int n_q, float* scores, int64_t ld,
+                                hipStream_t stream) {
+  const QueryDesc qd{q_seq, q_pos, c->seq_lens, c->n_seq,
+                     (int)std::min<int64_t>((int64_t)c->max_blocks_per_seq * c->block_size,
+                                            0x7fffffff),
+                     ld};
   if (phase == DSA_DECODE) {
     if (n_q <= kFlatMaxSeq) {
       // persistent grid: as many workgroups as fit on the device at once
@@ -446,7 +521,7 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
       }
       hipLaunchKernelGGL((index_score_decode_flat_kernel<H_IDX, D_IDX>), dim3(grid),
                          dim3(kThreads), 0, stream, c->k_idx, c->k_idx_row_stride, c->block_table,
-                         c->max_blocks_per_seq, c->block_size, c->seq_lens, n_q, q_idx, w,
+                         c->max_blocks_per_seq, c->block_size, c->num_blocks, qd, n_q, q_idx, w,
                          scores, ld);
     } else {
       // Chunk so that about 4096 workgroups cover n_q * ld positions.
@@ -454,58 +529,68 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
       int chunk = 1024;  // below this the per-workgroup query load dominates
       while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
       const int64_t nchunks = (ld + chunk - 1) / chunk;
-      if (nchunks > 0x7fffffff) return DSA_ERR_SHAPE;
+      if (nchunks > 0x7fffffff || n_q > 65535) return DSA_ERR_SHAPE;
       hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX>),
                          dim3((unsigned)nchunks, (unsigned)n_q), dim3(kThreads), 0, stream,
                          c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
-                         c->block_size, c->seq_lens, q_idx, w, scores, ld, chunk);
+                         c->block_size, c->num_blocks, qd, q_idx, w, scores, ld, chunk);
     }
   } else if constexpr (D_IDX == pf::kD && H_IDX % 16 == 0) {
-    const int64_t n_keys = (int64_t)pos0 + n_q;
-    const int64_t nchunks = (n_keys + pf::kChunk * pf::kKT - 1) / (pf::kChunk * pf::kKT);
+    // a workgroup covers up to 8192 keys of 16 queries: a whole row for
+    // positions below 8192, so the per-workgroup start (block-table
+    // lookups, q loads, first tile) is paid once per query block
+    const int64_t nchunks = (ld + pf::kChunk * pf::kKT - 1) / (pf::kChunk * pf::kKT);
     const int64_t nqb = ((int64_t)n_q + pf::kQB - 1) / pf::kQB;
     if (nqb > 65535) return DSA_ERR_SHAPE;
-    // a workgroup covers up to 8192 keys of 16 queries: a whole row for
-    // prefixes up to 8192, so the per-workgroup start (block-table lookups,
-    // q loads, first tile) is paid once per query block
     hipLaunchKernelGGL((index_score_prefill_kernel<H_IDX>), dim3((unsigned)nchunks, (unsigned)nqb),
                        dim3(pf::kThreads), 0, stream, c->k_idx, c->k_idx_row_stride,
-                       c->block_table + (int64_t)seq * c->max_blocks_per_seq, c->block_size,
-                       q_idx, w, n_q, pos0, scores, ld);
+                       c->block_table, c->max_blocks_per_seq, c->block_size, c->num_blocks, qd,
+                       q_idx, w, n_q, scores, ld);
   } else {
     constexpr int QB = 64, KB = 128;
-    const int64_t nkt = ((int64_t)pos0 + n_q + KB - 1) / KB;
+    const int64_t nkt = (ld + KB - 1) / KB;
     const int64_t nqb = ((int64_t)n_q + QB - 1) / QB;
+    if (nqb > 65535 || nkt > 0x7fffffff) return DSA_ERR_SHAPE;
     hipLaunchKernelGGL((index_score_prefill_tile_kernel<H_IDX, D_IDX, QB, KB>),
                        dim3((unsigned)nkt, (unsigned)nqb), dim3(kThreads), 0, stream, c->k_idx,
-                       c->k_idx_row_stride,
-                       c->block_table + (int64_t)seq * c->max_blocks_per_seq, c->block_size,
-                       q_idx, w, n_q, pos0, scores, ld);
+                       c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq, c->block_size,
+                       c->num_blocks, qd, q_idx, w, n_q, scores, ld);
   }
   return launch_status();
 }
 
 }  // namespace
+
+uint32_t take_bounds_error_index_score(hipStream_t stream) { return take_bounds_error(stream); }
+
 }  // namespace dsa
 
+extern "C" size_t dsa_index_score_ws(dsa_phase_t phase, int32_t n_q, int64_t ld) {
+  (void)phase;
+  (void)n_q;
+  (void)ld;
+  return 0;  // the index score needs no workspace
+}
+
 extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phase_t phase,
-                                        const uint16_t* q_idx, const float* w, int32_t n_q,
-                                        int32_t H_idx, int32_t prefill_seq, int32_t prefill_pos0,
-                                        float* scores, int64_t ld, hipStream_t stream) {
+                                        const uint16_t* q_idx, const float* w,
+                                        const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                                        int32_t H_idx, float* scores, int64_t ld, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
   using namespace dsa;
+  (void)workspace;
+  (void)workspace_bytes;
   dsa_status_t st = check_cache_common(cache);
   if (st != DSA_OK) return st;
   if (!cache->k_idx || !q_idx || !w || !scores) return DSA_ERR_NULL;
   if (phase != DSA_DECODE && phase != DSA_PREFILL) return DSA_ERR_SHAPE;
   if (n_q < 1 || ld < 1 || cache->k_idx_row_stride < cache->d_idx) return DSA_ERR_SHAPE;
-  if (phase == DSA_DECODE) {
+  if ((q_seq == nullptr) != (q_pos == nullptr)) return DSA_ERR_NULL;
+  if (!q_seq) {
+    // query i is the last cached token of sequence i
+    if (phase == DSA_PREFILL) return DSA_ERR_NULL;
     if (!cache->seq_lens) return DSA_ERR_NULL;
     if (n_q != cache->n_seq) return DSA_ERR_SHAPE;
-  } else {
-    if (prefill_seq < 0 || prefill_seq >= cache->n_seq || prefill_pos0 < 0) return DSA_ERR_SHAPE;
-    if ((int64_t)prefill_pos0 + n_q > ld) return DSA_ERR_SHAPE;
-    if ((int64_t)prefill_pos0 + n_q > (int64_t)cache->max_blocks_per_seq * cache->block_size)
-      return DSA_ERR_SHAPE;
   }
   const bool big = H_idx == 64 && cache->d_idx == 128;
   const bool small = H_idx == 4 && cache->d_idx == 32;
@@ -516,8 +601,7 @@ extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phas
   st = check_device();
   if (st != DSA_OK) return st;
   if (big)
-    return launch_index_score<64, 128>(cache, phase, q_idx, w, n_q, prefill_seq, prefill_pos0,
-                                       scores, ld, stream);
-  return launch_index_score<4, 32>(cache, phase, q_idx, w, n_q, prefill_seq, prefill_pos0, scores,
-                                   ld, stream);
+    return launch_index_score<64, 128>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores, ld,
+                                       stream);
+  return launch_index_score<4, 32>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores, ld, stream);
 }

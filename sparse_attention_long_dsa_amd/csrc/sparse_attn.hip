@@ -32,6 +32,8 @@
 // kernel; prefill has enough queries to fill the chip without splitting.
 #include <algorithm>
 
+#include <cmath>
+
 #include "attn_common.h"
 #include "host_util.h"
 
@@ -108,8 +110,7 @@ __global__ __launch_bounds__(2 * HB * kWave) void sparse_attn_kernel(
     const uint16_t* __restrict__ kv, int64_t kv_stride, const uint16_t* __restrict__ vpool,
     int64_t v_stride, const int32_t* __restrict__ block_table, int max_blocks, int bs,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ idx, int n_q, int K, int H,
-    int head_groups, const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0,
-    int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int head_groups, AttnQuery aq, int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
   using C = AttnCfg<HB, D_QK, D_V, SEP_V>;
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kTile * C::kRow];
@@ -122,9 +123,8 @@ __global__ __launch_bounds__(2 * HB * kWave) void sparse_attn_kernel(
   if (it.qi >= n_q) return;
   const int qi = it.qi, split = it.split;
   const int head0 = it.hg * 16 * HB;
-  const bool decode = seq_lens != nullptr;
-  const int seq = decode ? qi : prefill_seq;
-  const int n_cand = decode ? seq_lens[qi] : pos0 + qi + 1;
+  const int seq = aq.seq(qi);
+  const int n_cand = aq.count(qi);
   const int count = min(K, n_cand);
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
   const int32_t* sel = idx + (int64_t)qi * K;
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(2 * HB * kWave) void sparse_attn_kernel(
   // physical pool rows of every kept position of this block (-1: none)
   for (int r = threadIdx.x; r < (t_end - t_begin) * kTile; r += C::kThreads) {
     const int g = t_begin * kTile + r;
-    const int pos = g < count ? sel[g] : -1;
-    trows[r] = pos >= 0 ? (int32_t)paged_row(bt_row, bs, pos) : -1;
+    const int pos = g < count ? aq.kept(sel[g], n_cand) : -1;
+    trows[r] = pos >= 0 ? (int32_t)paged_row(bt_row, bs, pos, aq.num_blocks) : -1;
   }
 
   // q as the B operand of S^T: dims 32*ks + 8*grp .. +7 of this lane's head
@@ -336,11 +336,13 @@ Family family_of(const dsa_paged_cache_t* c, int H) {
 }
 
 dsa_status_t check_attn_args(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx,
-                             int n_q, int H, int K, const uint16_t* out, Family* fam) {
+                             int n_q, int H, int K, float sm_scale, const uint16_t* out,
+                             Family* fam) {
   dsa_status_t st = check_cache_common(c);
   if (st != DSA_OK) return st;
   if (!c->kv || !q || !idx || !out) return DSA_ERR_NULL;
   if (n_q < 1 || H < 1 || K < 1 || K > 2048) return DSA_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return DSA_ERR_SHAPE;
   if (c->kv_row_stride < c->d_qk) return DSA_ERR_SHAPE;
   if (c->v && c->v_row_stride < c->d_v) return DSA_ERR_SHAPE;
   if (!c->v && c->d_v > c->d_qk) return DSA_ERR_SHAPE;
@@ -354,14 +356,14 @@ dsa_status_t check_attn_args(const dsa_paged_cache_t* c, const uint16_t* q, cons
 
 template <int HB, int D_QK, int D_V, bool SEP_V>
 void launch_attn(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q, int H,
-                 int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale, uint16_t* out,
-                 float* lse, float* part_o, float* part_lse, SplitPlan plan, hipStream_t stream) {
+                 int K, AttnQuery aq, float sm_scale, uint16_t* out, float* lse, float* part_o,
+                 float* part_lse, SplitPlan plan, hipStream_t stream) {
   const int head_groups = (H + 16 * HB - 1) / (16 * HB);
   const int64_t blocks = ((int64_t)n_q + 7) / 8 * 8 * head_groups * plan.n_splits;
   hipLaunchKernelGGL((sparse_attn_kernel<HB, D_QK, D_V, SEP_V>), dim3((unsigned)blocks),
                      dim3(2 * HB * kWave), 0, stream, c->kv, c->kv_row_stride, c->v,
                      c->v_row_stride, c->block_table, c->max_blocks_per_seq, c->block_size, q,
-                     idx, n_q, K, H, head_groups, seq_lens, seq, pos0, plan.tiles_per_split,
+                     idx, n_q, K, H, head_groups, aq, plan.tiles_per_split,
                      sm_scale * kLog2e, out, lse, part_o, part_lse, plan.n_splits);
   if (plan.n_splits > 1)
     hipLaunchKernelGGL((attn_combine_kernel<D_V, float>), dim3(n_q * H), dim3(128), 0, stream, part_o,
@@ -384,6 +386,16 @@ size_t part_o_bytes(int B, int H, int d_v, SplitPlan p) {
   return (elems * (latent_shape(H, d_v) ? 2 : 4) + 255) / 256 * 256;
 }
 
+AttnQuery attn_query(const dsa_paged_cache_t* c, const int32_t* seq_lens, const int32_t* q_seq,
+                     const int32_t* q_pos) {
+  return AttnQuery{seq_lens, q_seq, q_pos, c->n_seq,
+                   (int)std::min<int64_t>((int64_t)c->max_blocks_per_seq * c->block_size,
+                                          0x7fffffff),
+                   c->num_blocks};
+}
+
+uint32_t take_bounds_error_small(hipStream_t stream) { return take_bounds_error(stream); }
+
 }  // namespace
 }  // namespace dsa
 
@@ -403,7 +415,7 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
                                                size_t workspace_bytes, hipStream_t stream) {
   using namespace dsa;
   Family fam;
-  dsa_status_t st = check_attn_args(cache, q, idx, B, H, K, out, &fam);
+  dsa_status_t st = check_attn_args(cache, q, idx, B, H, K, sm_scale, out, &fam);
   if (st != DSA_OK) return st;
   if (!cache->seq_lens) return DSA_ERR_NULL;
   if (B != cache->n_seq) return DSA_ERR_SHAPE;
@@ -415,37 +427,46 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
   const SplitPlan plan = decode_plan(B, H, K, cache->d_v);
   float* part_lse =
       need ? (float*)((char*)workspace + part_o_bytes(B, H, cache->d_v, plan)) : nullptr;
+  const AttnQuery aq = attn_query(cache, cache->seq_lens, nullptr, nullptr);
   if (fam == kLatent)
-    launch_latent(cache, q, idx, B, K, cache->seq_lens, 0, 0, sm_scale, out, lse,
-                  (uint16_t*)workspace, part_lse, plan, stream);
+    launch_latent(cache, q, idx, B, K, aq, sm_scale, out, lse, (uint16_t*)workspace, part_lse,
+                  plan, stream);
   else
-    launch_attn<1, 64, 64, true>(cache, q, idx, B, H, K, cache->seq_lens, 0, 0, sm_scale, out,
-                                 lse, (float*)workspace, part_lse, plan, stream);
+    launch_attn<1, 64, 64, true>(cache, q, idx, B, H, K, aq, sm_scale, out, lse,
+                                 (float*)workspace, part_lse, plan, stream);
   return launch_status();
 }
 
 extern "C" dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t* cache,
-                                                const uint16_t* q, const int32_t* idx, int32_t T,
-                                                int32_t H, int32_t K, int32_t seq, int32_t pos0,
-                                                float sm_scale, uint16_t* out, float* lse,
-                                                hipStream_t stream) {
+                                                const uint16_t* q, const int32_t* q_seq,
+                                                const int32_t* q_pos, const int32_t* idx,
+                                                int32_t T, int32_t H, int32_t K, float sm_scale,
+                                                uint16_t* out, float* lse, hipStream_t stream) {
   using namespace dsa;
   Family fam;
-  dsa_status_t st = check_attn_args(cache, q, idx, T, H, K, out, &fam);
+  dsa_status_t st = check_attn_args(cache, q, idx, T, H, K, sm_scale, out, &fam);
   if (st != DSA_OK) return st;
-  if (seq < 0 || seq >= cache->n_seq || pos0 < 0) return DSA_ERR_SHAPE;
-  if ((int64_t)pos0 + T > (int64_t)cache->max_blocks_per_seq * cache->block_size)
-    return DSA_ERR_SHAPE;
+  if (!q_seq || !q_pos) return DSA_ERR_NULL;
   st = check_device();
   if (st != DSA_OK) return st;
   const SplitPlan one{1, (K + kTile - 1) / kTile};
+  const AttnQuery aq = attn_query(cache, nullptr, q_seq, q_pos);
   if (fam == kLatent)
-    launch_latent(cache, q, idx, T, K, nullptr, seq, pos0, sm_scale, out, lse, nullptr, nullptr,
-                  one, stream);
+    launch_latent(cache, q, idx, T, K, aq, sm_scale, out, lse, nullptr, nullptr, one, stream);
   else
-    launch_attn<1, 64, 64, true>(cache, q, idx, T, H, K, nullptr, seq, pos0, sm_scale, out, lse,
-                                 nullptr, nullptr, one, stream);
+    launch_attn<1, 64, 64, true>(cache, q, idx, T, H, K, aq, sm_scale, out, lse, nullptr,
+                                 nullptr, one, stream);
   return launch_status();
+}
+
+extern "C" dsa_status_t dsa_check_device_errors(hipStream_t stream) {
+  using namespace dsa;
+  if (!kCheckBounds) return DSA_ERR_UNSUPPORTED;
+  const uint32_t e = take_bounds_error_small(stream) | take_bounds_error_latent(stream) |
+                     take_bounds_error_index_score(stream) | take_bounds_error_topk(stream) |
+                     take_bounds_error_cache_write(stream);
+  if (e & 0x80000000u) return DSA_ERR_HIP;
+  return e ? DSA_ERR_BOUNDS : DSA_OK;
 }
 
 extern "C" const char* dsa_status_string(dsa_status_t s) {
@@ -457,6 +478,7 @@ extern "C" const char* dsa_status_string(dsa_status_t s) {
     case DSA_ERR_WORKSPACE: return "workspace is missing or smaller than required";
     case DSA_ERR_DEVICE: return "the current device is not a usable gfx950";
     case DSA_ERR_HIP: return "a HIP launch failed";
+    case DSA_ERR_BOUNDS: return "device data out of range (block table, lengths, positions or indices)";
   }
   return "unknown status";
 }

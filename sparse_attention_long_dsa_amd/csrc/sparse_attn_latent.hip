@@ -146,8 +146,7 @@ __device__ __forceinline__ u32x4 load_vt32(const uint16_t* tile, int c0, int ks,
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     const uint16_t* __restrict__ kv, int64_t kv_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, const uint16_t* __restrict__ q, const int32_t* __restrict__ idx,
-    int n_q, int K, const int32_t* __restrict__ seq_lens, int prefill_seq, int pos0,
-    int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int n_q, int K, AttnQuery aq, int tiles_per_split, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int n_splits) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kBufs][kBufBytes / 2];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kPElems];
@@ -158,13 +157,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   // blocks of one query share an XCD (same block id modulo 8)
   const int b = blockIdx.x;
   const int j = b >> 3;
-  const bool decode = seq_lens != nullptr;
-  // prefill rows grow with the position: the longest go first
+  const bool decode = aq.decode();
+  // prefill rows usually grow with the query index: the latest go first
   const int qraw = (j / n_splits) * 8 + (b & 7), split = j % n_splits;
   const int qi = decode ? qraw : n_q - 1 - qraw;
   if (qi >= n_q || qi < 0) return;
-  const int seq = decode ? qi : prefill_seq;
-  const int n_cand = decode ? seq_lens[qi] : pos0 + qi + 1;
+  const int seq = aq.seq(qi);
+  const int n_cand = aq.count(qi);
   const int count = min(K, n_cand);
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
   const int32_t* sel = idx + (int64_t)qi * K;
@@ -186,13 +185,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   // still in flight.
   constexpr int kPer = kMaxTiles * kTile / kThreads;
   const int n_rows = (t_end - t_begin) * kTile;
-  const int32_t row_safe = (int32_t)bt_row[0] * bs;
+  const int32_t row_safe = (int32_t)checked_block(bt_row[0], aq.num_blocks) * bs;
   int32_t pos_r[kPer], blk_r[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int r = (int)threadIdx.x + kThreads * i;
     const int g = t_begin * kTile + r;
-    pos_r[i] = r < n_rows && g < count ? sel[g] : -1;
+    pos_r[i] = r < n_rows && g < count ? aq.kept(sel[g], n_cand) : -1;
   }
   bf16x8 qf[kKS];
   {
@@ -206,7 +205,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   // token: finite data) with weight 0.
   {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) blk_r[i] = pos_r[i] >= 0 ? bt_row[pos_r[i] / bs] : 0;
+    for (int i = 0; i < kPer; ++i)
+      blk_r[i] = pos_r[i] >= 0 ? checked_block(bt_row[pos_r[i] / bs], aq.num_blocks) : 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int r = (int)threadIdx.x + kThreads * i;
@@ -287,8 +287,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
     u32x4 ph;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w], scale_log2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + 2 * w + 1], scale_log2, -m_use));
+      const float p0 = __builtin_amdgcn_exp2f(sv[8 * ks + 2 * w] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(sv[8 * ks + 2 * w + 1] - m_use);
       psum += p0 + p1;
       ph[w] = pack_f16x2(p0, p1);
     }
@@ -368,6 +368,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
           if (next && ks < kWaveBlocks) load_block(ks);
         }
         mfma_result_fence(s);
+        // logits in the exp2 domain before the maximum is taken, so that any
+        // finite scale (zero and negative ones included) gives the true
+        // maximum; masked slots become -inf after scaling (weight 0)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] *= scale_log2;
         const uint32_t vm = tvalid[t - t_begin];
         if (vm != 0xffffffffu) {
 #pragma unroll
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
       float mt = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[v]);
-      mt = halves_max(mt) * scale_log2;
+      mt = halves_max(mt);
       if (have_s && m_base == -INFINITY) m_base = mt;
       if (have_s) m_seen = fmaxf(m_seen, mt);
       redo |= have_s && mt > m_base + kMaxExp;
@@ -481,14 +486,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
 }  // namespace latent
 }  // namespace
 
+uint32_t take_bounds_error_latent(hipStream_t stream) { return take_bounds_error(stream); }
+
 void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t* idx, int n_q,
-                   int K, const int32_t* seq_lens, int seq, int pos0, float sm_scale,
-                   uint16_t* out, float* lse, uint16_t* part_o, float* part_lse, SplitPlan plan,
-                   hipStream_t stream) {
+                   int K, AttnQuery aq, float sm_scale, uint16_t* out, float* lse,
+                   uint16_t* part_o, float* part_lse, SplitPlan plan, hipStream_t stream) {
   const int64_t blocks = ((int64_t)n_q + 7) / 8 * 8 * plan.n_splits;
   hipLaunchKernelGGL(latent::sparse_attn_latent_kernel, dim3((unsigned)blocks),
                      dim3(latent::kThreads), 0, stream, c->kv, c->kv_row_stride, c->block_table,
-                     c->max_blocks_per_seq, c->block_size, q, idx, n_q, K, seq_lens, seq, pos0,
+                     c->max_blocks_per_seq, c->block_size, q, idx, n_q, K, aq,
                      plan.tiles_per_split, sm_scale * kLog2e, out, lse, part_o, part_lse,
                      plan.n_splits);
   if (plan.n_splits > 1)

@@ -53,8 +53,14 @@ constexpr int kListCap = 12288;     // list entries the merge step holds in LDS
 constexpr int kSample = 8192;       // sampled keys per long row
 constexpr int kMaxChunks = 4096;    // ld <= kMaxChunks * kChunk
 
-__device__ __forceinline__ int row_count(const int32_t* n_valid, int causal_base, int row) {
-  return n_valid ? n_valid[row] : causal_base + row + 1;
+__device__ __forceinline__ int row_count(const int32_t* n_valid, int causal_base, int row,
+                                         int64_t ld) {
+  const int n = n_valid ? n_valid[row] : causal_base + row + 1;
+  if (kCheckBounds && (n < 0 || n > ld)) {  // device data: checked in debug builds
+    raise_error(kErrLength);
+    return 0;
+  }
+  return n;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(
   __shared__ uint32_t keys[MAXN];
   __shared__ uint32_t sh[Block<T>::kShWords];
   const int row = blockIdx.x;
-  const int n = row_count(n_valid, causal_base, row);
+  const int n = row_count(n_valid, causal_base, row, ld);
   int32_t* out = idx + (int64_t)row * K;
   if (n <= K) {
     write_all(n, K, out, T);
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kSampleThreads) void topk_sample_kernel(
   constexpr int T = kSampleThreads, R = kSample / T;
   __shared__ uint32_t sh[Block<T>::kShWords];
   const int row = blockIdx.x;
-  const int n = row_count(n_valid, causal_base, row);
+  const int n = row_count(n_valid, causal_base, row, ld);
   if (n <= K) return;
   if (n <= kListCap) {  // the whole row fits the merge step's list
     if (threadIdx.x == 0) ws.lower[row] = 0u;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
       for (int e = 0; e < 4; ++e) v[4 * j + e] = src[min((int64_t)(p + e), ld - 1)];
     }
   }
-  const int n = row_count(n_valid, causal_base, row);
+  const int n = row_count(n_valid, causal_base, row, ld);
   if (n <= K || s0 >= n) return;
   const int s1 = min(s0 + kChunk, n);
   const uint32_t lower = ws.lower[row];
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
   __shared__ uint32_t off[kMaxChunks + 1];  // list offset of each chunk, then the total
   __shared__ uint32_t sh[Block<T>::kShWords];
   const int row = blockIdx.x;
-  const int n = row_count(n_valid, causal_base, row);
+  const int n = row_count(n_valid, causal_base, row, ld);
   int32_t* out = idx + (int64_t)row * K;
   if (n <= K) {
     write_all(n, K, out, T);
@@ -515,6 +521,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
 }
 
 }  // namespace
+
+uint32_t take_bounds_error_topk(hipStream_t stream) { return take_bounds_error(stream); }
+
 }  // namespace dsa
 
 extern "C" size_t dsa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t K) {

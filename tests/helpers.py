@@ -36,9 +36,9 @@ def gpu_prefill(dc, pos0=0, T=None, seq=0):
     """Causal prefill of positions pos0 .. pos0+T-1 (queries are those rows of dc.q)."""
     wl = dc.wl
     T = wl.seq_lens[0] - pos0 if T is None else T
-    step = dsa.PrefillStep(cache_of(dc), T, wl.H, wl.topk, wl.d_v, pos0=pos0)
+    step = dsa.PrefillStep(cache_of(dc), T, wl.H, wl.topk, wl.d_v, pos0=pos0, seq=seq)
     step(dc.q[pos0:pos0 + T].contiguous(), dc.q_idx[pos0:pos0 + T].contiguous(),
-         dc.w[pos0:pos0 + T].contiguous(), wl.sm_scale, seq=seq)
+         dc.w[pos0:pos0 + T].contiguous(), wl.sm_scale)
     torch.cuda.synchronize()
     return step
 
@@ -101,18 +101,24 @@ def assert_topk_consistent(scores, idx, n_valid, K):
         assert torch.equal(kept_ties, ties[: kept_ties.numel()])
 
 
-def oracle_decode_sampled(wl, seqs):
-    """Oracle scores, Top-K, attention for decode queries of the listed
-    sequences, each computed from a private per-sequence pool."""
+def oracle_decode_rows(wl, seqs):
+    """Oracle scores, Top-K and attention of the decode queries of the listed
+    sequences, each from that sequence's own pools: its indexer keys in a
+    private paged pool, its kept K/V rows in a compact pool."""
     res = {}
     for b in seqs:
         L = wl.seq_lens[b]
         lbt, k_idx, _, _ = dsa_synth.host_sequence_pools(wl, b)
         q, q_idx, w = dsa_synth.host_query_rows(wl, b, 1)
         sc = oracle.index_score(k_idx, lbt, wl.block_size, q_idx, w, [0], [L - 1], ld=L)
+        del k_idx
         idx = oracle.topk(sc, [L], wl.topk)
-        _, _, kv, v = dsa_synth.host_sequence_pools(wl, b, kv_positions=idx[0])
-        out, lse = oracle.sparse_attn(kv, v, lbt, wl.block_size, q, [0], idx, wl.sm_scale,
-                                      d_v=wl.d_v)
+        table, kv, v = dsa_synth.host_kept_pool(wl, b, idx[0])
+        out, lse = oracle.sparse_attn(kv, v, table, 1, q, [0], idx, wl.sm_scale, d_v=wl.d_v)
         res[b] = (sc[0], idx[0], out[0], lse[0])
     return res
+
+
+def attention_margin(mx, mn):
+    """How much of the attention bars an error uses (fractions of 1e-2 / 1e-3)."""
+    return mx / ATOL_MAX, mn / ATOL_MEAN

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         assert L.dsa_status_string(code)
     assert L.dsa_status_string(99) == b"unknown status"
 
@@ -55,28 +55,38 @@ def cache(**kw):
     return dsa.PagedCache(**c)
 
 
-def score(L, c, phase=dsa.DSA_DECODE, q=FAKE, w=FAKE, n_q=2, H=64, seq=0, pos0=0, out=FAKE, ld=256):
-    return L.dsa_index_score(ctypes.byref(c), phase, q, w, n_q, H, seq, pos0, out, ld, None)
+def score(L, c, phase=dsa.DSA_DECODE, q=FAKE, w=FAKE, q_seq=None, q_pos=None, n_q=2, H=64,
+          out=FAKE, ld=256):
+    return L.dsa_index_score(ctypes.byref(c), phase, q, w, q_seq, q_pos, n_q, H, out, ld, None, 0,
+                             None)
 
 
 def test_index_score_validation(L):
+    assert L.dsa_index_score_ws(dsa.DSA_DECODE, 64, 1 << 17) == 0    # no workspace needed
+    assert L.dsa_index_score_ws(dsa.DSA_PREFILL, 8192, 8192) == 0
     assert score(L, cache(), q=None) == 1
     assert score(L, cache(k_idx=None)) == 1
     assert score(L, cache(block_table=None)) == 1
-    assert score(L, cache(seq_lens=None)) == 1
-    assert L.dsa_index_score(None, 1, FAKE, FAKE, 2, 64, 0, 0, FAKE, 256, None) == 1
-    assert score(L, cache(), n_q=3) == 2                    # decode: n_q must equal n_seq
+    assert score(L, cache(seq_lens=None)) == 1                # decode without per-query arrays
+    assert L.dsa_index_score(None, 1, FAKE, FAKE, None, None, 2, 64, FAKE, 256, None, 0,
+                             None) == 1
+    assert score(L, cache(), q_seq=FAKE) == 1                 # one array without the other
+    assert score(L, cache(), q_pos=FAKE) == 1
+    assert score(L, cache(), phase=dsa.DSA_PREFILL) == 1      # prefill needs both arrays
+    assert score(L, cache(), n_q=3) == 2                      # decode: n_q must equal n_seq
+    assert score(L, cache(), n_q=3, q_seq=FAKE, q_pos=FAKE) == 5   # ... unless per-query arrays
     assert score(L, cache(), ld=0) == 2
     assert score(L, cache(), phase=7) == 2
-    assert score(L, cache(), phase=dsa.DSA_PREFILL, n_q=200, ld=256, pos0=100) == 2  # past ld
-    assert score(L, cache(), phase=dsa.DSA_PREFILL, seq=2) == 2
     assert score(L, cache(), H=32) == 3
     assert score(L, cache(d_idx=64, k_idx_row_stride=64)) == 3
     assert score(L, cache(k_idx_row_stride=100)) == 2        # stride below width
     assert score(L, cache()) == 5                            # well formed: no gfx950 here
+    assert score(L, cache(seq_lens=None), q_seq=FAKE, q_pos=FAKE) == 5
+    assert score(L, cache(), phase=dsa.DSA_PREFILL, n_q=200, q_seq=FAKE, q_pos=FAKE) == 5
     assert score(L, cache(d_idx=32, k_idx_row_stride=32), H=4) == 5
     assert score(L, cache(k_idx=FAKE + 8)) == 3              # 16-byte alignment
     assert score(L, cache(), q=FAKE + 4) == 3
+    assert score(L, cache(block_size=8)) == 3                # 16-position key groups
 
 
 def test_topk_validation(L):
@@ -109,14 +119,28 @@ def test_attention_validation(L):
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 4096, 0.1, FAKE, None, FAKE, ws, None) == 2
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws - 1, None) == 4
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 5
+    # any finite softmax scale is accepted (zero and negative too); inf / nan are not
+    for scale in (0.0, -0.5, 1e30):
+        assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, scale, FAKE, None, FAKE, ws,
+                   None) == 5
+    for scale in (float("inf"), float("-inf"), float("nan")):
+        assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, scale, FAKE, None, FAKE, ws,
+                   None) == 2
+        assert pre(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 100, 128, 2048, scale, FAKE, None,
+                   None) == 2
     sep = cache(v=FAKE, v_row_stride=64, d_qk=64, d_v=64, kv_row_stride=64)
     assert dec(ctypes.byref(sep), FAKE, FAKE, 2, 8, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 5
     assert dec(ctypes.byref(cache(v=FAKE, v_row_stride=512)), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE,
                None, FAKE, ws, None) == 3                    # latent shape wants V inside K rows
-    assert pre(ctypes.byref(c), FAKE, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 5
-    assert pre(ctypes.byref(c), FAKE, FAKE, 300, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 2
-    assert pre(ctypes.byref(c), FAKE, FAKE, 100, 128, 2048, 5, 0, 0.1, FAKE, None, None) == 2
-    assert pre(ctypes.byref(c), None, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 1
+    assert pre(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 100, 128, 2048, 0.1, FAKE, None,
+               None) == 5
+    assert pre(ctypes.byref(c), FAKE, None, FAKE, FAKE, 100, 128, 2048, 0.1, FAKE, None,
+               None) == 1                                   # per-query arrays are required
+    assert pre(ctypes.byref(c), FAKE, FAKE, None, FAKE, 100, 128, 2048, 0.1, FAKE, None,
+               None) == 1
+    assert pre(ctypes.byref(c), None, FAKE, FAKE, FAKE, 100, 128, 2048, 0.1, FAKE, None,
+               None) == 1
+    assert pre(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 0, 128, 2048, 0.1, FAKE, None, None) == 2
     # 16-byte alignment of the vector-loaded buffers
     for bad in (dict(kv=FAKE + 2),):
         assert dec(ctypes.byref(cache(**bad)), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE,
@@ -124,7 +148,20 @@ def test_attention_validation(L):
     assert dec(ctypes.byref(c), FAKE + 8, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE, ws, None) == 3
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE + 4, None, FAKE, ws, None) == 3
     assert dec(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, FAKE + 4, ws, None) == 3
-    assert pre(ctypes.byref(c), FAKE + 2, FAKE, 100, 128, 2048, 0, 0, 0.1, FAKE, None, None) == 3
+    assert pre(ctypes.byref(c), FAKE + 2, FAKE, FAKE, FAKE, 100, 128, 2048, 0.1, FAKE, None,
+               None) == 3
+
+
+def test_device_error_check(L):
+    # release build: no checks compiled in
+    assert L.dsa_check_device_errors(None) == 3
+    # the debug build exports the same symbols; without a GPU its calls stop
+    # at the device check like the release build's
+    if not os.path.exists(dsa.DEBUG_LIB_PATH):
+        dsa.build(debug=True)
+    D = dsa.debug_lib()
+    assert score(D, cache()) == 5
+    assert score(D, cache(), q=None) == 1
 
 
 def test_cache_write_validation(L):

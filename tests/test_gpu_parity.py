@@ -349,3 +349,147 @@ def test_attention_skips_negative_indices():
     assert np.all(np.isneginf(lg[2]))
     np.testing.assert_allclose(lg[:2], lse[:2], atol=1e-2)
     say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+
+
+# ----------------------------------------------------------------------------- per-query calls
+
+def _dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _check_queries(wl, q_seq, q_pos, sm_scale=None, rel=False):
+    """One prefill-path call (index score, Top-K, attention) over arbitrary
+    queries (q_seq[i], q_pos[i]) of a multi-sequence cache, against the oracle."""
+    sm_scale = wl.sm_scale if sm_scale is None else sm_scale
+    q_seq = np.asarray(q_seq, np.int32)
+    q_pos = np.asarray(q_pos, np.int32)
+    T = len(q_seq)
+    say(f"[queries] {wl.name}: {T} queries over sequences {sorted(set(q_seq.tolist()))}, "
+        f"scale {sm_scale}")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    q, q_idx, w = dsa_synth.host_query_rows(wl, 0, T)
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    step = dsa.PrefillStep(cache, T, wl.H, wl.topk, wl.d_v, q_seq=torch.from_numpy(q_seq).cuda(),
+                           q_pos=torch.from_numpy(q_pos).cuda())
+    step(_dev_bf16(q), _dev_bf16(q_idx), torch.from_numpy(w).cuda(), sm_scale)
+    torch.cuda.synchronize()
+    ld = step.scores.shape[1]
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos, ld=ld)
+    idx = oracle.topk(sc, q_pos + 1, wl.topk)
+    out, lse = oracle.sparse_attn(hc.kv, hc.v, hc.block_table, wl.block_size, q, q_seq, idx,
+                                  sm_scale, d_v=wl.d_v)
+    g_sc = step.scores.cpu().numpy()
+    for i in range(T):
+        assert np.array_equal(g_sc[i, :q_pos[i] + 1], sc[i, :q_pos[i] + 1]), f"scores row {i}"
+    np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
+    mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name, rel=rel)
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+    return dc, step, (sc, idx, out, lse)
+
+
+def test_prefill_call_with_chunks_of_two_sequences():
+    # positions 300..690 of sequence 0, then 0..499 of sequence 1: the query
+    # block 384..399 holds both sequences (the index kernel's per-sequence pass)
+    wl = dsa_synth.latent("two_seq_prefill", "decode", [700, 500], seed=51, topk=256)
+    q_seq = [0] * 391 + [1] * 500
+    q_pos = list(range(300, 691)) + list(range(500))
+    _check_queries(wl, q_seq, q_pos)
+
+
+def test_small_family_prefill_call_with_two_sequences():
+    wl = dsa_synth.small_mqa("two_seq_small", "decode", [333, 200], seed=52, topk=64,
+                             block_size=16)
+    q_seq = [0] * 100 + [1] * 150 + [0] * 30
+    q_pos = list(range(233, 333)) + list(range(50, 200)) + list(range(30))
+    _check_queries(wl, q_seq, q_pos)
+
+
+def test_several_decode_queries_per_sequence():
+    # the decode index kernel with per-query arrays: the last three positions
+    # of every sequence (e.g. several draft tokens), attention by the
+    # per-query (prefill) path
+    wl = dsa_synth.latent("multi_query_decode", "decode", [3000, 17000, 40000], seed=53,
+                          topk=2048)
+    say(f"[decode, 3 queries per sequence] {wl.name}")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    q_seq = np.repeat(np.arange(3, dtype=np.int32), 3)
+    q_pos = np.array([L - 3 + j for L in wl.seq_lens for j in range(3)], np.int32)
+    T = len(q_seq)
+    q, q_idx, w = dsa_synth.host_query_rows(wl, 0, T)
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    ld = (max(wl.seq_lens) + 63) // 64 * 64
+    d_seq, d_pos = torch.from_numpy(q_seq).cuda(), torch.from_numpy(q_pos).cuda()
+    scores = dsa.index_score(cache, _dev_bf16(q_idx), torch.from_numpy(w).cuda(), dsa.DSA_DECODE,
+                             q_seq=d_seq, q_pos=d_pos, ld=ld)
+    g_idx = dsa.topk(scores, wl.topk, n_valid=d_pos + 1)
+    o, l = dsa.sparse_attn_prefill(cache, _dev_bf16(q), d_seq, d_pos, g_idx, wl.sm_scale)
+    torch.cuda.synchronize()
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos, ld=ld)
+    idx = oracle.topk(sc, q_pos + 1, wl.topk)
+    out, lse = oracle.sparse_attn(hc.kv, None, hc.block_table, wl.block_size, q, q_seq, idx,
+                                  wl.sm_scale, d_v=wl.d_v)
+    g_sc = scores.cpu().numpy()
+    for i in range(T):
+        assert np.array_equal(g_sc[i, :q_pos[i] + 1], sc[i, :q_pos[i] + 1]), f"scores row {i}"
+    np.testing.assert_array_equal(g_idx.cpu().numpy(), idx)
+    mx, mn = assert_attention(o, l, out, lse, wl.name)
+    say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0 / 24.0])
+def test_latent_zero_and_negative_softmax_scale(scale):
+    # the softmax scale may be any finite value: 0 gives equal weights, a
+    # negative one favours the lowest logits (decode and prefill kernels)
+    wl = dsa_synth.latent("scale_decode", "decode", [900, 5000, 20000], seed=54, topk=2048)
+    wl = dataclasses.replace(wl, sm_scale=scale)
+    check_decode(wl)
+    wp = dsa_synth.latent("scale_prefill", "decode", [600], seed=55, topk=256)
+    _check_queries(wp, [0] * 300, list(range(300, 600)), sm_scale=scale)
+
+
+def test_debug_build_flags_bad_device_data():
+    """The DSA_DEBUG_BOUNDS build checks the device data the host never reads.
+    The pool holds one block more than the cache description declares, so
+    the planted bad values address real memory in every build."""
+    wl = dsa_synth.latent("debug_bounds", "decode", [3000, 20000], seed=56, topk=512)
+    say(f"[debug build] {wl.name}")
+    D = dsa.debug_lib()
+    dc = dsa_synth.device_case(wl)
+    nb = wl.pool_blocks
+    kv = torch.cat([dc.kv, torch.zeros_like(dc.kv[:1])]).contiguous()
+    kidx = torch.cat([dc.k_idx, torch.zeros_like(dc.k_idx[:1])]).contiguous()
+    cache = dsa.Cache(kv, kidx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    cache.c.num_blocks = nb  # the extra block lies outside the description
+    st = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
+    # clean data: no error, and the same bits as the release build
+    st(dc.q, dc.q_idx, dc.w, wl.sm_scale, library=D)
+    assert dsa.check_device_errors(library=D) == 0
+    dbg = (st.idx.clone(), st.out.clone())
+    st(dc.q, dc.q_idx, dc.w, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dbg[0], st.idx) and torch.equal(dbg[1], st.out)
+    assert dsa.check_device_errors() == 3  # release build: nothing checked
+    # a block-table entry outside [0, num_blocks)
+    bt = dc.block_table.clone()
+    bt[1, 5] = nb
+    cache_bad = dsa.Cache(kv, kidx, bt, dc.seq_lens, d_v=wl.d_v)
+    cache_bad.c.num_blocks = nb
+    st.cache = cache_bad
+    st(dc.q, dc.q_idx, dc.w, wl.sm_scale, library=D)
+    assert dsa.check_device_errors(library=D) == 7
+    assert dsa.check_device_errors(library=D) == 0  # the record was cleared
+    # a kept index past its row's candidate count
+    idx = dbg[0].clone()
+    idx[0, 3] = wl.seq_lens[0]
+    dsa.sparse_attn_decode(cache, dc.q, idx, wl.sm_scale, library=D)
+    assert dsa.check_device_errors(library=D) == 7
+    # a sequence length beyond the block table
+    lens = dc.seq_lens.clone()
+    lens[0] = wl.max_blocks * wl.block_size + 1
+    cache_len = dsa.Cache(kv, kidx, dc.block_table, lens, d_v=wl.d_v)
+    cache_len.c.num_blocks = nb
+    dsa.index_score(cache_len, dc.q_idx, dc.w, dsa.DSA_DECODE, out=st.scores, library=D)
+    assert dsa.check_device_errors(library=D) == 7
+    say("   ok: clean data passes, bad block / index / length are flagged")
