@@ -175,6 +175,21 @@ dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t *cache, const uint16
                                     float sm_scale, uint16_t *out, float *lse, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* Sparse attention, decode path, allocating nothing: for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and results as dsa_sparse_attn_decode, but the split partial
+ * results live in a static device array of the library: 48 MiB (50331648
+ * bytes) per GPU, held from the library's load until the process ends.
+ * Sizes whose dsa_sparse_attn_decode_workspace_size exceeds that return
+ * DSA_ERR_WORKSPACE before anything is launched.  Every call on one GPU uses
+ * the same array, so calls that overlap on one GPU (concurrent streams,
+ * threads) race; calls ordered on one stream do not. */
+dsa_status_t dsa_sparse_attn_decode_static(const dsa_paged_cache_t *cache, const uint16_t *q,
+                                           const int32_t *idx, int32_t B, int32_t H, int32_t K,
+                                           float sm_scale, uint16_t *out, float *lse,
+                                           hipStream_t stream);
+
 /* Sparse attention, prefill path (page 1, section 3 item (3): many queries,
  * compute bound).  Query t belongs to sequence q_seq[t] at position
  * q_pos[t] (int32 [T] device arrays, 0 <= q_seq[t] < n_seq, 0 <= q_pos[t] <

@@ -121,13 +121,15 @@ def _configure(L):
     L.dsa_sparse_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     L.dsa_sparse_attn_decode_workspace_size.restype = sz
     L.dsa_sparse_attn_decode.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.dsa_sparse_attn_decode_static.argtypes = [pc, vp, vp, i32, i32, i32, f32, vp, vp, vp]
     L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp]
     L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
     L.dsa_check_device_errors.argtypes = [vp]
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
-    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode, L.dsa_sparse_attn_prefill,
-              L.dsa_cache_write, L.dsa_check_device_errors):
+    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode,
+              L.dsa_sparse_attn_decode_static, L.dsa_sparse_attn_prefill, L.dsa_cache_write,
+              L.dsa_check_device_errors):
         f.restype = i32
     return L
 
@@ -309,6 +311,28 @@ def sparse_attn_decode(cache: Cache, q, idx, sm_scale: float, out=None, lse=None
                                     K, float(sm_scale), out.data_ptr(), _ptr(lse),
                                     workspace.data_ptr(), workspace.numel(), _stream(stream)),
            "dsa_sparse_attn_decode", L)
+    return out, lse
+
+
+def sparse_attn_decode_static(cache: Cache, q, idx, sm_scale: float, out=None, lse=None,
+                              want_lse: bool = True, stream=None, library=None):
+    """dsa_sparse_attn_decode_static: as sparse_attn_decode, with the split
+    partials in the library's static device array (no workspace)."""
+    import torch
+
+    L = library or lib()
+    _need(q, torch.bfloat16, "q")
+    _need(idx, torch.int32, "idx")
+    B, H, _ = q.shape
+    K = idx.shape[1]
+    d_v = cache.c.d_v
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check(L.dsa_sparse_attn_decode_static(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(),
+                                           B, H, K, float(sm_scale), out.data_ptr(), _ptr(lse),
+                                           _stream(stream)), "dsa_sparse_attn_decode_static", L)
     return out, lse
 
 

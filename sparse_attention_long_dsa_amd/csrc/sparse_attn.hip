@@ -33,6 +33,7 @@
 #include <algorithm>
 
 #include <cmath>
+#include <mutex>
 
 #include "attn_common.h"
 #include "host_util.h"
@@ -396,6 +397,31 @@ AttnQuery attn_query(const dsa_paged_cache_t* c, const int32_t* seq_lens, const 
 
 uint32_t take_bounds_error_small(hipStream_t stream) { return take_bounds_error(stream); }
 
+// Scratch of the allocation-free decode entry point: the split partials live
+// in this file-scope device array (one copy per GPU, held until the process
+// ends).  Host code uses the per-device address from hipGetSymbolAddress,
+// never the array's name (a host-side stand-in).
+constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on the first call on
+// that device (with it current).
+dsa_status_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -435,6 +461,31 @@ extern "C" dsa_status_t dsa_sparse_attn_decode(const dsa_paged_cache_t* cache, c
     launch_attn<1, 64, 64, true>(cache, q, idx, B, H, K, aq, sm_scale, out, lse,
                                  (float*)workspace, part_lse, plan, stream);
   return launch_status();
+}
+
+extern "C" dsa_status_t dsa_sparse_attn_decode_static(const dsa_paged_cache_t* cache,
+                                                      const uint16_t* q, const int32_t* idx,
+                                                      int32_t B, int32_t H, int32_t K,
+                                                      float sm_scale, uint16_t* out, float* lse,
+                                                      hipStream_t stream) {
+  using namespace dsa;
+  Family fam;
+  dsa_status_t st = check_attn_args(cache, q, idx, B, H, K, sm_scale, out, &fam);
+  if (st != DSA_OK) return st;
+  if (!cache->seq_lens) return DSA_ERR_NULL;
+  if (B != cache->n_seq) return DSA_ERR_SHAPE;
+  const size_t need = dsa_sparse_attn_decode_workspace_size(B, H, K, cache->d_v);
+  if (need > kStaticScratchBytes) return DSA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != DSA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = static_scratch(&ws);
+    if (st != DSA_OK) return st;
+  }
+  // every split writes all of its partial result (zeros / -inf for an
+  // empty split), so nothing in the scratch needs clearing
+  return dsa_sparse_attn_decode(cache, q, idx, B, H, K, sm_scale, out, lse, ws, need, stream);
 }
 
 extern "C" dsa_status_t dsa_sparse_attn_prefill(const dsa_paged_cache_t* cache,

@@ -152,6 +152,21 @@ def test_attention_validation(L):
                None) == 3
 
 
+def test_static_decode_validation(L):
+    f = L.dsa_sparse_attn_decode_static
+    c = cache()
+    assert f(ctypes.byref(c), FAKE, FAKE, 2, 128, 2048, 0.1, FAKE, None, None) == 5  # fits
+    assert f(ctypes.byref(c), None, FAKE, 2, 128, 2048, 0.1, FAKE, None, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, 3, 128, 2048, 0.1, FAKE, None, None) == 2
+    # 200 queries x 2 splits of fp16 partials need more than the 48 MiB array
+    assert L.dsa_sparse_attn_decode_workspace_size(200, 128, 2048, 512) > 48 << 20
+    big = cache(n_seq=200)
+    assert f(ctypes.byref(big), FAKE, FAKE, 200, 128, 2048, 0.1, FAKE, None, None) == 4
+    assert L.dsa_sparse_attn_decode_workspace_size(64, 128, 2048, 512) <= 48 << 20
+    ok = cache(n_seq=64)
+    assert f(ctypes.byref(ok), FAKE, FAKE, 64, 128, 2048, 0.1, FAKE, None, None) == 5
+
+
 def test_device_error_check(L):
     # release build: no checks compiled in
     assert L.dsa_check_device_errors(None) == 3
