@@ -133,7 +133,7 @@ def probe_lib():
         raise RuntimeError(f"{dsa.PROBE_LIB} is missing: build it with __graft_entry__.build()")
     L = ctypes.CDLL(dsa.PROBE_LIB)
     L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                 ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_void_p]
     L.hbm_read_probe.restype = ctypes.c_int
     return L
 
@@ -165,7 +165,7 @@ class Timer:
         self.n_flush += 1
         self.flush_buf.fill_(self.n_flush & 0xFF)
         rc = self.probe.hbm_read_probe(self.read_buf.data_ptr(), FLUSH_BYTES,
-                                       self.sink.data_ptr(), 4096,
+                                       self.sink.data_ptr(), 4096, 0,
                                        ctypes.c_void_p(self.stream.cuda_stream))
         if rc != 0:
             raise RuntimeError(f"hbm_read_probe failed ({rc})")
@@ -323,13 +323,13 @@ def hbm_probe(log):
     buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     best = None
-    for grid in (1024, 2048, 4096, 8192):
+    for grid, nt in ((1024, 1), (2048, 1), (4096, 1), (8192, 1), (4096, 0)):
         sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
         times = []
         for rep in range(6):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            rc = L.hbm_read_probe(buf.data_ptr(), PROBE_BYTES, sink.data_ptr(), grid,
+            rc = L.hbm_read_probe(buf.data_ptr(), PROBE_BYTES, sink.data_ptr(), grid, nt,
                                   ctypes.c_void_p(stream.cuda_stream))
             b.record(stream)
             if rc != 0:
@@ -338,14 +338,15 @@ def hbm_probe(log):
             if rep > 0:
                 times.append(a.elapsed_time(b))
         gbs = PROBE_BYTES / (statistics.median(times) * 1e-3) / 1e9
-        log(f"hbm probe: grid {grid} x 256: {gbs:.0f} GB/s")
+        log(f"hbm probe: grid {grid} x 256, {'non-temporal' if nt else 'ordinary'} loads: "
+            f"{gbs:.0f} GB/s")
         if best is None or gbs > best[0]:
-            best = (gbs, grid)
+            best = (gbs, grid, nt)
     del buf
     torch.cuda.empty_cache()
     return {"kernel": "hbm_read_kernel (streaming read, 16 B a lane, 8 loads in flight)",
             "bytes": PROBE_BYTES, "gbs": round(best[0], 1), "grid_blocks": best[1],
-            "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
+            "nontemporal": bool(best[2]), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, budget_s, log):

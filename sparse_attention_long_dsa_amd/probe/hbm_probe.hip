@@ -17,6 +17,10 @@ constexpr int kInFlight = 8;  // 16-byte loads a lane keeps in flight
 // Thread t of the grid reads the 16-byte vectors t, t + N, t + 2N, ... (N =
 // all threads of the grid), kInFlight at a time, and folds them into one
 // word that is stored once (so the loads cannot be dropped).
+// NT: non-temporal loads (a hint not to keep the lines in the caches) for
+// the bandwidth figure; ordinary loads when the read is meant to fill the
+// caches with these (clean) lines.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restrict__ src,
                                                             int64_t n_vec, uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -25,7 +29,8 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restr
   for (; i + (kInFlight - 1) * stride < n_vec; i += kInFlight * stride) {
     u32x4 v[kInFlight];
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kInFlight; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -40,11 +45,16 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restr
 
 // Reads `bytes` (a multiple of 16) from device buffer `src` once; `sink`
 // receives one word per thread of the grid (grid_blocks * 256 words).
-// Returns 0, or 1 for bad arguments, 2 when the launch fails.
+// nontemporal != 0: non-temporal loads.  Returns 0, or 1 for bad arguments,
+// 2 when the launch fails.
 extern "C" int hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int grid_blocks,
-                              hipStream_t stream) {
+                              int nontemporal, hipStream_t stream) {
   if (!src || !sink || bytes < 16 || bytes % 16 != 0 || grid_blocks < 1) return 1;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(grid_blocks), dim3(kThreads), 0, stream,
-                     (const u32x4*)src, bytes / 16, sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(grid_blocks), dim3(kThreads), 0, stream,
+                       (const u32x4*)src, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(grid_blocks), dim3(kThreads), 0, stream,
+                       (const u32x4*)src, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
