@@ -52,6 +52,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_long_dsa_amd", "csrc")
 # kernel -> the sources its counter figures were taken on
 KERNEL_SOURCES = {
     "index_score_decode": ["index_score.hip", "common.h"],
+    "topk_fused": ["topk.hip", "common.h"],
     "sparse_attn_latent": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
     "attn_combine": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
     "topk": ["topk.hip", "common.h"],
@@ -170,7 +171,9 @@ class Timer:
         if rc != 0:
             raise RuntimeError(f"hbm_read_probe failed ({rc})")
 
-    def run(self, calls, steps, warmup):
+    def run(self, calls, steps, warmup, breakdown=None):
+        """Pass A times `calls` as whole steps; pass B times each call of
+        `breakdown` (default: `calls`) on its own within a step."""
         torch = self.torch
         for _ in range(warmup):
             for c in calls:
@@ -189,17 +192,18 @@ class Timer:
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
         step_ms = [a.elapsed_time(b) for a, b in ev]
         # pass B: per-call breakdown
-        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        parts = breakdown or calls
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
                for _ in range(steps)]
         for i in range(steps):
             self.flush()
             evb[i][0].record(self.stream)
-            for j, c in enumerate(calls):
+            for j, c in enumerate(parts):
                 c()
                 evb[i][j + 1].record(self.stream)
         torch.cuda.synchronize()
         per_call = [statistics.median(e[j].elapsed_time(e[j + 1]) for e in evb)
-                    for j in range(len(calls))]
+                    for j in range(len(parts))]
         return {"median_ms": statistics.median(step_ms), "min_ms": min(step_ms),
                 "max_ms": max(step_ms), "wall_ms_incl_flush": wall_ms, "per_call_ms": per_call}
 
@@ -217,12 +221,17 @@ def bench_decode(n, timer, steps, warmup, log):
         f"{time.time() - t0:.1f}s")
     cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
     st = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v)
-    calls = [lambda: dsa.index_score(cache, dc.q_idx, dc.w, dsa.DSA_DECODE, out=st.scores),
-             lambda: dsa.topk(st.scores, wl.topk, n_valid=dc.seq_lens, out=st.idx,
-                              workspace=st.ws_topk),
-             lambda: dsa.sparse_attn_decode(cache, dc.q, st.idx, wl.sm_scale, out=st.out,
-                                            lse=st.lse, workspace=st.ws_attn)]
-    r = timer.run(calls, steps, warmup)
+
+    def stage(flags):
+        return lambda: dsa.index_topk_decode(cache, dc.q_idx, dc.w, wl.topk, st.scores, st.idx,
+                                             st.ws_topk, flags=flags)
+
+    attend = lambda: st.attend(dc.q, wl.sm_scale)  # noqa: E731
+    # the step: the fused index score + Top-K call, then the attention call;
+    # breakdown: the fused call's two launches timed apart (same arguments)
+    r = timer.run([stage(0), attend], steps, warmup,
+                  breakdown=[stage(dsa.DSA_INDEX_TOPK_SCORE_ONLY),
+                             stage(dsa.DSA_INDEX_TOPK_SELECT_ONLY), attend])
     step_bytes, index_bytes = decode_bytes(wl)
     ms = r["median_ms"]
     idx_ms, topk_ms, attn_ms = r["per_call_ms"]
@@ -238,7 +247,7 @@ def bench_decode(n, timer, steps, warmup, log):
         "index_gbs": round(index_bytes / (idx_ms * 1e-3) / 1e9, 1),
         "attn_gbs": round(attn_bytes(wl) / (attn_ms * 1e-3) / 1e9, 1),
     }
-    del dc, cache, st, calls
+    del dc, cache, st
     torch.cuda.empty_cache()
     return res, wl
 

@@ -156,6 +156,47 @@ dsa_status_t dsa_topk(const float *scores, int64_t ld, int32_t n_q, int32_t K,
                       const int32_t *n_valid, int32_t causal_base, int32_t *idx, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* Flags of dsa_index_topk_decode. */
+#define DSA_TOPK_SEED_PREVIOUS 1
+#define DSA_INDEX_TOPK_SCORE_ONLY 2   /* run only the first launch (scores, group maxima) */
+#define DSA_INDEX_TOPK_SELECT_ONLY 4  /* run only the second launch, on the workspace of a
+                                         SCORE_ONLY call with the same arguments */
+
+/* Workspace bytes dsa_index_topk_decode needs: for ld <= 262144 two fp32
+ * group maxima per 16 positions of a row and one word per row (about
+ * n_q * ld / 2 bytes); above, the long-row Top-K's (about 8 * n_q * ld). */
+size_t dsa_index_topk_decode_ws(int32_t n_q, int64_t ld, int32_t K);
+
+/* Index score and Top-K fused for decode rows (page 1, section 3 item (1):
+ * block-wise scoring, intra-block reduction and cross-block merge; item
+ * (3): decode reuses the previous step's index structure).  Computes what
+ * dsa_index_score (DSA_DECODE) followed by dsa_topk computes -- the same
+ * scores, written to `scores` [n_q, ld], and the same kept positions,
+ * written to `idx` [n_q, K] (ascending, ties to the lower position, -1
+ * padded) -- for the queries that q_seq / q_pos (or, both NULL, the last
+ * token of each sequence, n_q == n_seq) describe, with row i's candidates
+ * 0 .. pos_i.  The index kernel also writes, for every 16-position group,
+ * its two largest scores into the workspace; the K-th largest of those
+ * bounds the row's K-th largest score from below, so the Top-K step reads
+ * only the groups that reach the bound, then selects exactly among them.
+ * Rows capacities ld above 262144 (a million-token context) take the
+ * long-row selection of dsa_topk instead, which spreads a row over many
+ * workgroups.  The call makes two launches (the long-row path four);
+ * flags DSA_INDEX_TOPK_SCORE_ONLY and DSA_INDEX_TOPK_SELECT_ONLY run the
+ * index score, resp. the selection, on its own (for timing each apart).
+ * DSA_TOPK_SEED_PREVIOUS tries each row's K-th largest score of the
+ * previous call on this workspace as the bound (ld <= 262144; used only
+ * when it is verified to be one; results never depend on it).  ld must be a multiple
+ * of 4 and at most 2^24; scores must be 16-byte aligned; 1 <= K <= 2048.
+ * Workspace: dsa_index_topk_decode_ws(n_q, ld, K) bytes, 16-byte aligned,
+ * no initialisation needed (with DSA_TOPK_SEED_PREVIOUS it must hold the
+ * previous call's results for the same rows to be of use). */
+dsa_status_t dsa_index_topk_decode(const dsa_paged_cache_t *cache, const uint16_t *q_idx,
+                                   const float *w, const int32_t *q_seq, const int32_t *q_pos,
+                                   int32_t n_q, int32_t H_idx, int32_t K, float *scores,
+                                   int64_t ld, int32_t *idx, int32_t flags, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes dsa_sparse_attn_decode needs (split-K partial results). */
 size_t dsa_sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t K, int32_t d_v);
 

@@ -32,6 +32,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 DSA_PREFILL, DSA_DECODE = 0, 1
+DSA_TOPK_SEED_PREVIOUS, DSA_INDEX_TOPK_SCORE_ONLY, DSA_INDEX_TOPK_SELECT_ONLY = 1, 2, 4
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
           4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP", 7: "DSA_ERR_BOUNDS"}
 
@@ -115,6 +116,10 @@ def _configure(L):
     L.dsa_index_score.argtypes = [pc, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp, sz, vp]
     L.dsa_index_score_ws.argtypes = [i32, i32, i64]
     L.dsa_index_score_ws.restype = sz
+    L.dsa_index_topk_decode_ws.argtypes = [i32, i64, i32]
+    L.dsa_index_topk_decode_ws.restype = sz
+    L.dsa_index_topk_decode.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, vp, i64, vp, i32, vp,
+                                        sz, vp]
     L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
     L.dsa_topk_workspace_size.restype = sz
     L.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, sz, vp]
@@ -127,7 +132,7 @@ def _configure(L):
     L.dsa_check_device_errors.argtypes = [vp]
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
-    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_sparse_attn_decode,
+    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_index_topk_decode, L.dsa_sparse_attn_decode,
               L.dsa_sparse_attn_decode_static, L.dsa_sparse_attn_prefill, L.dsa_cache_write,
               L.dsa_check_device_errors):
         f.restype = i32
@@ -246,6 +251,32 @@ def index_score(cache: Cache, q_idx, w, phase: int, q_seq=None, q_pos=None,
                              _ptr(q_seq), _ptr(q_pos), n_q, H_idx, out.data_ptr(), out.shape[1],
                              None, 0, _stream(stream)), "dsa_index_score", L)
     return out
+
+
+def index_topk_workspace(n_q: int, ld: int, K: int, device="cuda"):
+    import torch
+
+    n = lib().dsa_index_topk_decode_ws(n_q, ld, K)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def index_topk_decode(cache: Cache, q_idx, w, K: int, scores, idx, workspace, q_seq=None,
+                      q_pos=None, flags: int = 0, stream=None, library=None):
+    """dsa_index_topk_decode: scores [n_q, ld] and kept positions [n_q, K] in
+    one call (index kernel with group maxima, then one Top-K kernel)."""
+    import torch
+
+    L = library or lib()
+    _need(q_idx, torch.bfloat16, "q_idx")
+    _need(w, torch.float32, "w")
+    _need(scores, torch.float32, "scores")
+    _need(idx, torch.int32, "idx")
+    n_q, H_idx, _ = q_idx.shape
+    _check(L.dsa_index_topk_decode(ctypes.byref(cache.c), q_idx.data_ptr(), w.data_ptr(),
+                                   _ptr(q_seq), _ptr(q_pos), n_q, H_idx, K, scores.data_ptr(),
+                                   scores.shape[1], idx.data_ptr(), flags, workspace.data_ptr(),
+                                   workspace.numel(), _stream(stream)), "dsa_index_topk_decode", L)
+    return scores, idx
 
 
 def check_device_errors(stream=None, library=None) -> int:
@@ -385,28 +416,46 @@ def cache_write(cache: Cache, seq, pos, kv_new, k_idx_new, v_new=None, stream=No
 
 class DecodeStep:
     """One decode step over a batch (index score -> Top-K -> sparse attention)
-    with every buffer allocated once up front."""
+    with every buffer allocated once up front.  fused=True runs the index
+    score and Top-K as one dsa_index_topk_decode call; fused=False as the two
+    separate calls.  seed=True passes DSA_TOPK_SEED_PREVIOUS from the second
+    call on (the previous step's per-row threshold as a hint)."""
 
     def __init__(self, cache: Cache, B: int, H: int, H_idx: int, K: int, ld: int, d_v: int,
-                 device="cuda"):
+                 device="cuda", fused: bool = True, seed: bool = False):
         import torch
 
-        self.cache, self.K = cache, K
+        self.cache, self.K, self.fused, self.seed = cache, K, fused, seed
         ld = (ld + 63) // 64 * 64  # aligned score rows: 16-byte loads in Top-K
         self.scores = torch.empty((B, ld), dtype=torch.float32, device=device)
         self.idx = torch.empty((B, K), dtype=torch.int32, device=device)
         self.out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
-        self.ws_topk = topk_workspace(B, ld, K, device)
+        self.ws_topk = (index_topk_workspace(B, ld, K, device) if fused else
+                        topk_workspace(B, ld, K, device))
         self.ws_attn = decode_workspace(B, H, K, d_v, device)
+        self.calls = 0
+
+    def select(self, q_idx, w, stream=None, library=None):
+        """Index score and Top-K of the step (self.scores, self.idx)."""
+        c = self.cache
+        if self.fused:
+            flags = DSA_TOPK_SEED_PREVIOUS if self.seed and self.calls > 0 else 0
+            index_topk_decode(c, q_idx, w, self.K, self.scores, self.idx, self.ws_topk,
+                              flags=flags, stream=stream, library=library)
+        else:
+            index_score(c, q_idx, w, DSA_DECODE, out=self.scores, stream=stream, library=library)
+            topk(self.scores, self.K, n_valid=c.tensors[3], out=self.idx, workspace=self.ws_topk,
+                 stream=stream, library=library)
+        self.calls += 1
+
+    def attend(self, q, sm_scale: float, stream=None, library=None):
+        sparse_attn_decode(self.cache, q, self.idx, sm_scale, out=self.out, lse=self.lse,
+                           workspace=self.ws_attn, stream=stream, library=library)
 
     def __call__(self, q, q_idx, w, sm_scale: float, stream=None, library=None):
-        c = self.cache
-        index_score(c, q_idx, w, DSA_DECODE, out=self.scores, stream=stream, library=library)
-        topk(self.scores, self.K, n_valid=c.tensors[3], out=self.idx, workspace=self.ws_topk,
-             stream=stream, library=library)
-        sparse_attn_decode(c, q, self.idx, sm_scale, out=self.out, lse=self.lse,
-                           workspace=self.ws_attn, stream=stream, library=library)
+        self.select(q_idx, w, stream=stream, library=library)
+        self.attend(q, sm_scale, stream=stream, library=library)
         return self.out, self.lse
 
 

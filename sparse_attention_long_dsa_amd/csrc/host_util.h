@@ -45,4 +45,11 @@ __attribute__((visibility("hidden"))) uint32_t take_bounds_error_index_score(hip
 __attribute__((visibility("hidden"))) uint32_t take_bounds_error_topk(hipStream_t stream);
 __attribute__((visibility("hidden"))) uint32_t take_bounds_error_cache_write(hipStream_t stream);
 
+// The decode index score that also writes each 16-position group's two
+// largest scores (the fused index + Top-K call), in index_score.hip.
+__attribute__((visibility("hidden"))) dsa_status_t launch_index_score_decode_gmax(
+    const dsa_paged_cache_t* c, const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+    const int32_t* q_pos, int n_q, int H_idx, float* scores, int64_t ld, float* gm1, float* gm2,
+    int64_t ldg, hipStream_t stream);
+
 }  // namespace dsa

@@ -20,6 +20,7 @@
 // queries; the query block keeps its queries in registers over a long run
 // of key tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "host_util.h"
@@ -36,12 +37,41 @@ constexpr int kWaves = kThreads / kWave;
 // 64x128 operand sits in registers; the indexer keys stream HBM -> MFMA
 // operand registers with two register buffers, so one round's loads fly
 // while the previous round's MFMAs and epilogue run.
-template <int H_IDX, int D_IDX, int UNROLL>
+// The two largest of the 16 values held by the lanes of each 16-lane row
+// (as a multiset: a value held twice is both), in every lane of the row.
+// Each step merges two disjoint sets of lanes: pairs (quad xor 1), quads
+// (quad xor 2), half rows (lane i with 7 - i), halves (lane i with 15 - i).
+__device__ __forceinline__ void row_top2(float& a1, float& a2) {
+  auto step = [&](auto ctrl) {
+    constexpr int c = decltype(ctrl)::value;
+    const float b1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a1), c, 0xf, 0xf, false));
+    const float b2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a2), c, 0xf, 0xf, false));
+    const float lo = fminf(a1, b1);
+    a1 = fmaxf(a1, b1);
+    a2 = fmaxf(lo, fmaxf(a2, b2));
+  };
+  step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{});  // row_mirror
+}
+
+// Group maxima written by the fused decode path: for group g (positions
+// 16 g .. 16 g + 15 of a row) m1[g] is its largest score and m2[g] its
+// second largest (NaN when the group holds a single position).
+struct GroupMaxOut {
+  float* m1;
+  float* m2;
+  int64_t ldg;  // row stride of both arrays
+};
+
+template <int H_IDX, int D_IDX, int UNROLL, bool GMAX>
 __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx, int64_t k_stride,
                                               const int32_t* __restrict__ bt_row, int bs,
                                               int num_blocks, const uint16_t* __restrict__ q_row,
                                               const float* __restrict__ w_row,
-                                              float* __restrict__ out, int t0, int t1) {
+                                              float* __restrict__ out, float* __restrict__ gm1,
+                                              float* __restrict__ gm2, int t0, int t1) {
   constexpr int HT = (H_IDX + 15) / 16;  // 16-head tiles
   constexpr int KS = D_IDX / 32;         // 32-wide k-steps
   const int lane = threadIdx.x & (kWave - 1);
@@ -110,6 +140,16 @@ __device__ __forceinline__ void score_segment(const uint16_t* __restrict__ k_idx
       s = wave_sum_xor_16_32(s);
       const int tok = base + 16 * u + col;
       if (grp == 0 && tok >= t0 && tok < t1) out[tok] = s;
+      if constexpr (GMAX) {
+        // t0 is a multiple of 16 here: the group lies in [t0, t1) up to its tail
+        const int g0 = base + 16 * u;
+        float a1 = tok < t1 ? s : -INFINITY, a2 = -INFINITY;
+        row_top2(a1, a2);
+        if (lane == 0 && g0 < t1) {
+          gm1[g0 >> 4] = a1;
+          gm2[g0 >> 4] = t1 - g0 >= 2 ? a2 : __int_as_float(0x7fc00000);
+        }
+      }
     }
   };
 
@@ -159,20 +199,21 @@ struct QueryDesc {
 // each workgroup of a persistent grid takes one equal slice, whatever the
 // ragged lengths; the query is reloaded only where a slice crosses into the
 // next sequence.  Needs n_seq <= kFlatMaxSeq (prefix sums sit in LDS).
-template <int H_IDX, int D_IDX>
+template <int H_IDX, int D_IDX, bool GMAX>
 __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, int num_blocks, QueryDesc qd, int n_seq,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, GroupMaxOut gmo) {
   __shared__ int64_t cum[kFlatMaxSeq + 1];
   __shared__ int64_t wave_tot[kWaves];
-  // exclusive prefix of the lengths: per-thread runs, a scan across each
-  // wave's lanes, then the four wave totals
+  // exclusive prefix of the lengths in 16-position groups (slices start on
+  // a group boundary, so each group is scored by one workgroup): per-thread
+  // runs, a scan across each wave's lanes, then the four wave totals
   const int per = (n_seq + kThreads - 1) / kThreads;
   const int s0 = threadIdx.x * per, s1 = min(s0 + per, n_seq);
   int64_t run = 0;
-  for (int i = s0; i < s1; ++i) run += qd.count(i);
+  for (int i = s0; i < s1; ++i) run += (qd.count(i) + 15) >> 4;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int64_t incl = run;
 #pragma unroll
@@ -191,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
   run = base + incl - run;  // exclusive prefix of this thread's run
   for (int i = s0; i < s1; ++i) {
     cum[i] = run;
-    run += qd.count(i);
+    run += (qd.count(i) + 15) >> 4;
   }
   if (threadIdx.x == 0) cum[n_seq] = total_all;
   __syncthreads();
@@ -206,33 +247,33 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_decode_flat_kernel(
     if (cum[mid + 1] <= lo) b0 = mid + 1; else b1 = mid;
   }
   for (int b = b0; b < n_seq && cum[b] < hi; ++b) {
-    const int t0 = (int)max<int64_t>(lo - cum[b], 0);
-    const int t1 = (int)min<int64_t>(hi - cum[b], cum[b + 1] - cum[b]);
+    const int L = qd.count(b);
+    const int t0 = 16 * (int)max<int64_t>(lo - cum[b], 0);
+    const int t1 = (int)min<int64_t>(16 * (hi - cum[b]), L);
     if (t0 >= t1) continue;
-    score_segment<H_IDX, D_IDX, kUnroll>(
+    score_segment<H_IDX, D_IDX, kUnroll, GMAX>(
         k_idx, k_stride, block_table + (int64_t)qd.seq(b) * max_blocks, bs, num_blocks,
-        q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0,
-        t1);
+        q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX, scores + (int64_t)b * ld,
+        gmo.m1 + b * gmo.ldg, gmo.m2 + b * gmo.ldg, t0, t1);
   }
 }
 
 // Decode, one (sequence, chunk) per workgroup: for batches too wide for the
 // token-balanced kernel.
-template <int H_IDX, int D_IDX>
+template <int H_IDX, int D_IDX, bool GMAX>
 __global__ __launch_bounds__(kThreads) void index_score_decode_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, int num_blocks, QueryDesc qd,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+    float* __restrict__ scores, int64_t ld, int chunk, GroupMaxOut gmo) {
   const int b = blockIdx.y;
   const int L = qd.count(b);
-  const int t0 = blockIdx.x * chunk;
+  const int t0 = blockIdx.x * chunk;  // chunk is a multiple of 16
   if (t0 >= L) return;
-  score_segment<H_IDX, D_IDX, kUnroll>(k_idx, k_stride,
-                                       block_table + (int64_t)qd.seq(b) * max_blocks, bs,
-                                       num_blocks, q_idx + (int64_t)b * H_IDX * D_IDX,
-                                       w + (int64_t)b * H_IDX, scores + (int64_t)b * ld, t0,
-                                       min(t0 + chunk, L));
+  score_segment<H_IDX, D_IDX, kUnroll, GMAX>(
+      k_idx, k_stride, block_table + (int64_t)qd.seq(b) * max_blocks, bs, num_blocks,
+      q_idx + (int64_t)b * H_IDX * D_IDX, w + (int64_t)b * H_IDX, scores + (int64_t)b * ld,
+      gmo.m1 + b * gmo.ldg, gmo.m2 + b * gmo.ldg, t0, min(t0 + chunk, L));
 }
 
 // ---------------------------------------------------------------- prefill
@@ -494,11 +535,11 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
   }
 }
 
-template <int H_IDX, int D_IDX>
+template <int H_IDX, int D_IDX, bool GMAX>
 dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
                                 const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                                 const int32_t* q_pos, int n_q, float* scores, int64_t ld,
-                                hipStream_t stream) {
+                                GroupMaxOut gmo, hipStream_t stream) {
   const QueryDesc qd{q_seq, q_pos, c->seq_lens, c->n_seq,
                      (int)std::min<int64_t>((int64_t)c->max_blocks_per_seq * c->block_size,
                                             0x7fffffff),
@@ -506,7 +547,7 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
   if (phase == DSA_DECODE) {
     if (n_q <= kFlatMaxSeq) {
       // persistent grid: as many workgroups as fit on the device at once
-      static int grid_cache[64] = {0};
+      static int grid_cache[64] = {0};  // per device (one per GMAX instantiation)
       int dev = 0;
       (void)hipGetDevice(&dev);
       int grid = dev < 64 ? grid_cache[dev] : 0;
@@ -514,15 +555,16 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, index_score_decode_flat_kernel<H_IDX, D_IDX>, kThreads, 0) != hipSuccess)
+                &per_cu, index_score_decode_flat_kernel<H_IDX, D_IDX, GMAX>, kThreads, 0) !=
+                hipSuccess)
           return DSA_ERR_HIP;
         grid = std::max(1, cus * std::max(1, per_cu));
         if (dev < 64) grid_cache[dev] = grid;
       }
-      hipLaunchKernelGGL((index_score_decode_flat_kernel<H_IDX, D_IDX>), dim3(grid),
+      hipLaunchKernelGGL((index_score_decode_flat_kernel<H_IDX, D_IDX, GMAX>), dim3(grid),
                          dim3(kThreads), 0, stream, c->k_idx, c->k_idx_row_stride, c->block_table,
                          c->max_blocks_per_seq, c->block_size, c->num_blocks, qd, n_q, q_idx, w,
-                         scores, ld);
+                         scores, ld, gmo);
     } else {
       // Chunk so that about 4096 workgroups cover n_q * ld positions.
       int64_t per = (int64_t)n_q * ld / 4096;
@@ -530,11 +572,13 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
       while (chunk < 8192 && chunk * 2 <= per) chunk *= 2;
       const int64_t nchunks = (ld + chunk - 1) / chunk;
       if (nchunks > 0x7fffffff || n_q > 65535) return DSA_ERR_SHAPE;
-      hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX>),
+      hipLaunchKernelGGL((index_score_decode_kernel<H_IDX, D_IDX, GMAX>),
                          dim3((unsigned)nchunks, (unsigned)n_q), dim3(kThreads), 0, stream,
                          c->k_idx, c->k_idx_row_stride, c->block_table, c->max_blocks_per_seq,
-                         c->block_size, c->num_blocks, qd, q_idx, w, scores, ld, chunk);
+                         c->block_size, c->num_blocks, qd, q_idx, w, scores, ld, chunk, gmo);
     }
+  } else if constexpr (GMAX) {
+    return DSA_ERR_SHAPE;  // group maxima come from the decode kernels only
   } else if constexpr (D_IDX == pf::kD && H_IDX % 16 == 0) {
     // a workgroup covers up to 8192 keys of 16 queries: a whole row for
     // positions below 8192, so the per-workgroup start (block-table
@@ -562,6 +606,19 @@ dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
 }  // namespace
 
 uint32_t take_bounds_error_index_score(hipStream_t stream) { return take_bounds_error(stream); }
+
+dsa_status_t launch_index_score_decode_gmax(const dsa_paged_cache_t* c, const uint16_t* q_idx,
+                                            const float* w, const int32_t* q_seq,
+                                            const int32_t* q_pos, int n_q, int H_idx,
+                                            float* scores, int64_t ld, float* gm1, float* gm2,
+                                            int64_t ldg, hipStream_t stream) {
+  const GroupMaxOut gmo{gm1, gm2, ldg};
+  if (H_idx == 64 && c->d_idx == 128)
+    return launch_index_score<64, 128, true>(c, DSA_DECODE, q_idx, w, q_seq, q_pos, n_q, scores,
+                                             ld, gmo, stream);
+  return launch_index_score<4, 32, true>(c, DSA_DECODE, q_idx, w, q_seq, q_pos, n_q, scores, ld,
+                                         gmo, stream);
+}
 
 }  // namespace dsa
 
@@ -600,8 +657,10 @@ extern "C" dsa_status_t dsa_index_score(const dsa_paged_cache_t* cache, dsa_phas
   if (cache->block_size % 16 != 0) return DSA_ERR_UNSUPPORTED;        // 16-position groups
   st = check_device();
   if (st != DSA_OK) return st;
+  const GroupMaxOut none{nullptr, nullptr, 0};
   if (big)
-    return launch_index_score<64, 128>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores, ld,
-                                       stream);
-  return launch_index_score<4, 32>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores, ld, stream);
+    return launch_index_score<64, 128, false>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores,
+                                              ld, none, stream);
+  return launch_index_score<4, 32, false>(cache, phase, q_idx, w, q_seq, q_pos, n_q, scores, ld,
+                                          none, stream);
 }

@@ -520,6 +520,378 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
   }
 }
 
+// ================================================================ fused decode rows
+//
+// The Top-K half of dsa_index_topk_decode.  The index kernel has already
+// done the block-wise scoring: for every 16-position group g of a row it
+// wrote the group's largest score m1[g] and second largest m2[g].  One
+// workgroup per row then
+//   1. takes a value that at least K of the group maxima reach (the K-th
+//      largest, found to within 25% of K candidates): the maxima are scores
+//      of distinct positions, so at least K scores of the row reach it, it
+//      bounds the row's K-th largest score from below, and every kept
+//      position lies in a group whose maximum reaches it (intra-block
+//      reduction).  Rows of fewer than 4 K groups use both m1 and m2;
+//   2. lists, in position order, the groups that reach the bound, then the
+//      scores of those groups that reach it (ordered compaction; all loads
+//      coalesced: consecutive lanes read consecutive groups);
+//   3. runs the exact threshold search and ordered compaction on that list
+//      (cross-block merge).
+// A hint (the row's K-th largest key of an earlier call, kept in the
+// workspace) replaces step 1's search when at least K and at most 2 K of the
+// group maxima reach it.  When a list would overflow LDS the row is selected
+// exactly from global memory instead.  Rows of at most 16384 candidates are
+// selected whole, in registers.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedList = 12288;    // list entries held in LDS
+constexpr int kFusedGroups = 4096;   // candidate groups held in LDS
+constexpr int kFusedShort = 16384;   // rows up to this are selected whole
+constexpr int kMaxRounds = 16;       // 4 * kFusedGroups / kFusedThreads
+static_assert(4 * kFusedGroups / kFusedThreads == kMaxRounds, "expansion rounds");
+
+struct GroupMaxIn {
+  const float* m1;
+  const float* m2;
+  int64_t ldg;
+  uint32_t* tau;  // [n_q] K-th largest key of each row (written; read as a hint when seeded)
+  int seed;
+};
+
+__device__ __forceinline__ uint32_t key_or_empty(float f) {
+  return f == f ? float_key(f) : 0u;  // NaN marks "no value"
+}
+
+// Exact selection of a row straight from global memory (the fallback).
+template <int T>
+__device__ uint32_t select_row_global(Block<T>& blk, const float* __restrict__ src, uint32_t n,
+                                      uint32_t K, int32_t* __restrict__ out) {
+  uint32_t a = 0xffffffffu, o = 0u;
+  for (uint32_t e = threadIdx.x; e < n; e += T) {
+    const uint32_t k = float_key(src[e]);
+    a &= k;
+    o |= k;
+  }
+  auto wave_ge = [&](uint32_t c) {
+    uint32_t n_ge = 0;
+    for (uint32_t e = threadIdx.x; e < n; e += T) n_ge += float_key(src[e]) >= c ? 1u : 0u;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) n_ge += __shfl_xor(n_ge, off);
+    return n_ge;
+  };
+  const Threshold th = select_tau(blk, a, o, wave_ge, K);
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t gt_base = 0, eq_base = 0;
+  for (uint32_t e0 = 0; e0 < n; e0 += T) {
+    const uint32_t e = e0 + threadIdx.x;
+    const uint32_t k = e < n ? float_key(src[e]) : 0u;
+    const bool gt = e < n && k > th.tau;
+    const bool eq = e < n && k == th.tau;
+    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+    const uint32_t packed = (uint32_t)__popcll(mgt) | ((uint32_t)__popcll(meq) << 16);
+    uint32_t tot;
+    const uint32_t before = blk.prefix_excl(lane == 0 ? packed : 0u, &tot);
+    const uint32_t wave_gt = (__shfl(before, 0) & 0xffffu) + (uint32_t)__popcll(mgt & lanemask_lt(lane));
+    const uint32_t wave_eq = (__shfl(before, 0) >> 16) + (uint32_t)__popcll(meq & lanemask_lt(lane));
+    const uint32_t eq_rank = eq_base + wave_eq;
+    if (gt || (eq && eq_rank < th.need)) out[gt_base + wave_gt + min(eq_rank, th.need)] = (int32_t)e;
+    gt_base += tot & 0xffffu;
+    eq_base += tot >> 16;
+  }
+  return th.tau;
+}
+
+// Offsets of an ordered compaction whose items are laid out slot-major:
+// item (i, t) = slot i of thread t comes before (i, t + 1) and (i + 1, 0).
+// c[i]: the entries item (i, this thread) contributes; off[i] receives its
+// first entry's position; returns the total.  Slots i >= n_slots (uniform)
+// are ignored.  `sc` holds R * kFusedWaves + 1 words; two barriers.
+template <int R>
+__device__ uint32_t slot_major_offsets(const uint32_t (&c)[R], int n_slots, uint32_t (&off)[R],
+                                       uint32_t* sc) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint32_t incl[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i < n_slots) {
+    uint32_t x = c[i];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    incl[i] = x;
+    if (lane == kWave - 1) sc[i * kFusedWaves + wave] = x;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scan of the n_slots * 16 wave totals, in place
+    const int n = n_slots * kFusedWaves;
+    const int per = (n + kWave - 1) / kWave;
+    uint32_t run = 0;
+    for (int e = lane * per; e < min(n, lane * per + per); ++e) run += sc[e];
+    uint32_t x = run;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    uint32_t acc = x - run;
+    for (int e = lane * per; e < min(n, lane * per + per); ++e) {
+      const uint32_t v = sc[e];
+      sc[e] = acc;
+      acc += v;
+    }
+    if (lane == kWave - 1) sc[n] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < n_slots) off[i] = sc[i * kFusedWaves + wave] + incl[i] - c[i];
+  return sc[n_slots * kFusedWaves];
+}
+
+template <int RG>
+__global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ counts,
+    int count_add, int K, GroupMaxIn gm, int32_t* __restrict__ idx) {
+  constexpr int T = kFusedThreads;
+  __shared__ uint2 ent[kFusedList];
+  __shared__ uint32_t cg[kFusedGroups];
+  __shared__ uint32_t sc[kMaxRounds * kFusedWaves + 1];
+  __shared__ uint32_t sh[Block<T>::kShWords];
+  const int row = blockIdx.x;
+  // candidates 0 .. n - 1: the sequence length, or the query position + 1
+  const int n = row_count(counts, 0, row, ld - count_add) + count_add;
+  int32_t* out = idx + (int64_t)row * K;
+  if (n <= K) {
+    write_all(n, K, out, T);
+    return;
+  }
+  const float* src = scores + (int64_t)row * ld;
+  Block<T> blk(sh);
+
+  if (n <= kFusedShort) {  // the whole row in registers, 16 keys a thread
+    constexpr int R = kFusedShort / T;
+    uint32_t* keys = (uint32_t*)ent;
+    float v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) v[i] = src[min((int)threadIdx.x + T * i, n - 1)];
+    uint32_t k[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int p = threadIdx.x + T * i;
+      k[i] = p < n ? float_key(v[i]) : 0u;
+      if (p < n) keys[p] = k[i];
+    }
+    uint32_t a, o;
+    thread_and_or(k, a, o);
+    const Threshold th = select_tau(blk, a, o, RegCount<R>{k}, (uint32_t)K);
+    __syncthreads();
+    ordered_compact(blk, (uint32_t)n, th, [&](uint32_t e) { return make_uint2(keys[e], e); },
+                    out);
+    if (threadIdx.x == 0) gm.tau[row] = th.tau;
+    return;
+  }
+
+  // ---- 1. bound.  Group j = slot i * T + t of thread t (consecutive lanes
+  // read consecutive groups; rows have at most RG * T groups).
+  const int G = (n + 15) >> 4;
+  const int n_slots = (G + T - 1) / T;  // uniform
+  const bool two = G < 4 * K;           // both maxima of each group
+  const float* m1 = gm.m1 + (int64_t)row * gm.ldg;
+  const float* m2 = gm.m2 + (int64_t)row * gm.ldg;
+  uint32_t k1[RG], k2[RG];
+  {
+    float a1[RG], a2[RG];  // unconditional loads from clamped addresses, masked afterwards
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int j = min(i * T + (int)threadIdx.x, G - 1);
+      a1[i] = i < n_slots ? m1[j] : 0.f;
+      a2[i] = i < n_slots && two ? m2[j] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const bool live = i < n_slots && i * T + (int)threadIdx.x < G;
+      k1[i] = live ? key_or_empty(a1[i]) : 0u;
+      k2[i] = live && two ? key_or_empty(a2[i]) : 0u;
+    }
+  }
+  // keys >= c among the live slots (n_slots is uniform: no wasted ballots)
+  auto count_ge = [&](uint32_t c) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+      if (i < n_slots)
+        cnt += (uint32_t)__popcll(__ballot(k1[i] >= c)) + (uint32_t)__popcll(__ballot(k2[i] >= c));
+    return cnt;
+  };
+  uint32_t bound = 0;
+  bool have = false;
+  if (gm.seed) {  // a hint: valid if at least K maxima reach it, useful if at most 2 K do
+    const uint32_t hint = gm.tau[row];
+    if (hint != 0u) {
+      const uint32_t c = blk.sum_waves(count_ge(hint));
+      if (c >= (uint32_t)K && c <= 2u * (uint32_t)K) {
+        bound = hint;
+        have = true;
+      }
+    }
+  }
+  if (!have) {
+    // bitwise search for the K-th largest key, stopped once at most 5 K / 4
+    // keys reach the prefix (any value that K keys reach is a valid bound)
+    uint32_t a = 0xffffffffu, o = 0u;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      if (k1[i]) {
+        a &= k1[i];
+        o |= k1[i];
+      }
+      if (k2[i]) {
+        a &= k2[i];
+        o |= k2[i];
+      }
+    }
+    blk.and_or(a, o);
+    uint32_t prefix = a, diff = a ^ o;
+    const uint32_t stop = (uint32_t)K + (uint32_t)K / 4;
+    while (diff) {
+      const uint32_t bit = 1u << (31 - __clz(diff));
+      diff &= ~bit;
+      const uint32_t c = blk.sum_waves(count_ge(prefix | bit));
+      if (c >= (uint32_t)K) {
+        prefix |= bit;
+        if (c <= stop) break;
+      }
+    }
+    bound = prefix;
+  }
+
+  // ---- 2a. candidate groups (maximum >= bound), in position order
+  uint32_t off[RG], flag[RG];
+#pragma unroll
+  for (int i = 0; i < RG; ++i) flag[i] = i < n_slots && k1[i] >= bound && k1[i] != 0u ? 1u : 0u;
+  const uint32_t m_g = slot_major_offsets(flag, n_slots, off, sc);
+  const bool fit = m_g <= (uint32_t)kFusedGroups;
+  if (fit) {
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+      if (i < n_slots && flag[i]) cg[off[i]] = (uint32_t)(i * T + (int)threadIdx.x);
+  }
+  __syncthreads();
+
+  // ---- 2c. the listed groups' scores that reach the bound: item e = 4 c + v
+  // is quarter v (4 positions, one 16-byte load) of listed group c.  Rounds
+  // of T items go in batches of 4 (loads of a batch in flight together); a
+  // count pass, one ordered prefix, then a write pass that loads again.
+  uint32_t m = 0;
+  if (fit) {
+    constexpr int R = kMaxRounds, B = 4;
+    const int rounds = (int)((4 * m_g + T - 1) / T);  // uniform, <= 16
+    auto load_batch = [&](int rb, float4 (&x)[B], int (&p0)[B]) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int r = rb + b;
+        const uint32_t e = (uint32_t)(r * T) + threadIdx.x;
+        const uint32_t c = min(e >> 2, m_g - 1);
+        p0[b] = r < rounds && e < 4 * m_g ? (int)cg[c] * 16 + 4 * (int)(e & 3u) : n;
+        // p0 < ld implies p0 + 3 < ld (ld is a multiple of 4)
+        x[b] = *(const float4*)(src + min(p0[b], (int)ld - 4));
+      }
+    };
+    uint32_t cnt[R], eoff[R];
+#pragma unroll
+    for (int rb = 0; rb < R; rb += B) {
+      float4 x[B];
+      int p0[B];
+      if (rb < rounds) load_batch(rb, x, p0);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        cnt[rb + b] = 0;
+        if (rb < rounds) {
+          const float xv[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            cnt[rb + b] += p0[b] + q < n && float_key(xv[q]) >= bound ? 1u : 0u;
+        }
+      }
+    }
+    m = slot_major_offsets(cnt, rounds, eoff, sc);
+    if (m <= (uint32_t)kFusedList) {
+#pragma unroll
+      for (int rb = 0; rb < R; rb += B) {
+        if (rb < rounds) {
+          float4 x[B];
+          int p0[B];
+          load_batch(rb, x, p0);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const float xv[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
+            uint32_t at = eoff[rb + b];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t k = float_key(xv[q]);
+              if (p0[b] + q < n && k >= bound) ent[at++] = make_uint2(k, (uint32_t)(p0[b] + q));
+            }
+          }
+        }
+      }
+    }
+  }
+  if (!fit || m > (uint32_t)kFusedList) {
+    const uint32_t tau = select_row_global(blk, src, (uint32_t)n, (uint32_t)K, out);
+    if (threadIdx.x == 0) gm.tau[row] = tau;
+    return;
+  }
+  __syncthreads();
+
+  // ---- 3. exact search and ordered compaction over the list (m >= K);
+  // thread t holds entries t, t + T, ...
+  constexpr int RL = kFusedList / T;
+  const int rl = (int)((m + T - 1) / T);  // uniform
+  uint32_t kl[RL];
+#pragma unroll
+  for (int i = 0; i < RL; ++i) {
+    const uint32_t e = (uint32_t)(i * T) + threadIdx.x;
+    kl[i] = i < rl && e < m ? ent[e].x : 0u;
+  }
+  uint32_t a, o;
+  thread_and_or(kl, a, o);
+  auto list_ge = [&](uint32_t c) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < RL; ++i)
+      if (i < rl) cnt += (uint32_t)__popcll(__ballot(kl[i] >= c));
+    return cnt;
+  };
+  const Threshold th = select_tau(blk, a, o, list_ge, (uint32_t)K);
+  ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
+  if (threadIdx.x == 0) gm.tau[row] = th.tau;
+}
+
+// Workspace of dsa_index_topk_decode: the group maxima and the per-row keys.
+struct FusedWs {
+  float* m1;
+  float* m2;
+  uint32_t* tau;
+  int64_t ldg;
+};
+
+size_t fused_ws_bytes(int n_q, int64_t ld, FusedWs* ws, void* base) {
+  const int64_t ldg = (ld + 15) / 16;
+  const size_t gm = align_up((size_t)n_q * ldg * 4, 256);
+  const size_t t = align_up((size_t)n_q * 4, 256);
+  if (ws) {
+    char* p = (char*)base;
+    ws->m1 = (float*)p;
+    ws->m2 = (float*)(p + gm);
+    ws->tau = (uint32_t*)(p + 2 * gm);
+    ws->ldg = ldg;
+  }
+  return 2 * gm + t;
+}
+
 }  // namespace
 
 uint32_t take_bounds_error_topk(hipStream_t stream) { return take_bounds_error(stream); }
@@ -571,5 +943,110 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t ld, int32_t n_q, i
                        ld, n_valid, causal_base, K, ws);
   hipLaunchKernelGGL(topk_merge_kernel, dim3(n_q), dim3(kRowThreads), 0, stream, scores, ld,
                      n_valid, causal_base, K, ws, idx);
+  return launch_status();
+}
+
+namespace dsa {
+namespace {
+// Rows of more than this many positions are selected by the three-launch
+// path (sample, chunks, merge), whose chunk step spreads a row over many
+// workgroups; one workgroup per row is faster below it.
+constexpr int64_t kFusedMaxLd = 262144;
+}  // namespace
+}  // namespace dsa
+
+namespace dsa {
+namespace {
+// counts[i] = q_pos[i] + 1 (the long-row path's candidate counts)
+__global__ void counts_from_positions_kernel(const int32_t* __restrict__ q_pos,
+                                             int32_t* __restrict__ counts, int n_q) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_q) counts[i] = q_pos[i] + 1;
+}
+size_t long_path_ws_bytes(int n_q, int64_t ld) {
+  return long_ws_bytes(n_q, ld, nullptr, nullptr) + align_up((size_t)n_q * 4, 256);
+}
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_index_topk_decode_ws(int32_t n_q, int64_t ld, int32_t K) {
+  if (n_q < 1 || ld < 1 || K < 1) return 0;
+  if (ld > dsa::kFusedMaxLd) return dsa::long_path_ws_bytes(n_q, ld);
+  return dsa::fused_ws_bytes(n_q, ld, nullptr, nullptr);
+}
+
+extern "C" dsa_status_t dsa_index_topk_decode(const dsa_paged_cache_t* cache, const uint16_t* q_idx,
+                                              const float* w, const int32_t* q_seq,
+                                              const int32_t* q_pos, int32_t n_q, int32_t H_idx,
+                                              int32_t K, float* scores, int64_t ld, int32_t* idx,
+                                              int32_t flags, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+  using namespace dsa;
+  dsa_status_t st = check_cache_common(cache);
+  if (st != DSA_OK) return st;
+  if (!cache->k_idx || !q_idx || !w || !scores || !idx) return DSA_ERR_NULL;
+  if ((q_seq == nullptr) != (q_pos == nullptr)) return DSA_ERR_NULL;
+  if (!q_seq && !cache->seq_lens) return DSA_ERR_NULL;
+  if (n_q < 1 || ld < 1 || K < 1 || K > 2048) return DSA_ERR_SHAPE;
+  if (!q_seq && n_q != cache->n_seq) return DSA_ERR_SHAPE;
+  if (ld % 4 != 0 || ld > (int64_t)1 << 24 || cache->k_idx_row_stride < cache->d_idx)
+    return DSA_ERR_SHAPE;
+  if ((flags & ~(DSA_TOPK_SEED_PREVIOUS | DSA_INDEX_TOPK_SCORE_ONLY |
+                 DSA_INDEX_TOPK_SELECT_ONLY)) != 0 ||
+      (flags & DSA_INDEX_TOPK_SCORE_ONLY && flags & DSA_INDEX_TOPK_SELECT_ONLY))
+    return DSA_ERR_SHAPE;
+  const bool big = H_idx == 64 && cache->d_idx == 128;
+  const bool small = H_idx == 4 && cache->d_idx == 32;
+  if (!big && !small) return DSA_ERR_UNSUPPORTED;
+  if (cache->k_idx_row_stride % 8 != 0 || cache->block_size % 16 != 0) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(cache->k_idx) || !aligned16(q_idx) || !aligned16(scores))
+    return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa_index_topk_decode_ws(n_q, ld, K);
+  if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DSA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != DSA_OK) return st;
+  if (ld > kFusedMaxLd) {
+    // long rows: the plain index score, then the three-launch Top-K (the
+    // per-row hint is not used on this path)
+    const size_t topk_bytes = long_ws_bytes(n_q, ld, nullptr, nullptr);
+    int32_t* counts = (int32_t*)((char*)workspace + topk_bytes);
+    if (!(flags & DSA_INDEX_TOPK_SELECT_ONLY)) {
+      st = dsa_index_score(cache, DSA_DECODE, q_idx, w, q_seq, q_pos, n_q, H_idx, scores, ld,
+                           nullptr, 0, stream);
+      if (st != DSA_OK || (flags & DSA_INDEX_TOPK_SCORE_ONLY)) return st;
+    }
+    if (q_pos) {
+      hipLaunchKernelGGL(counts_from_positions_kernel, dim3((n_q + 255) / 256), dim3(256), 0,
+                         stream, q_pos, counts, n_q);
+      st = launch_status();
+      if (st != DSA_OK) return st;
+    }
+    return dsa_topk(scores, ld, n_q, K, q_pos ? counts : cache->seq_lens, 0, idx, workspace,
+                    topk_bytes, stream);
+  }
+  FusedWs ws;
+  fused_ws_bytes(n_q, ld, &ws, workspace);
+  if (!(flags & DSA_INDEX_TOPK_SELECT_ONLY)) {
+    st = launch_index_score_decode_gmax(cache, q_idx, w, q_seq, q_pos, n_q, H_idx, scores, ld,
+                                        ws.m1, ws.m2, ws.ldg, stream);
+    if (st != DSA_OK || (flags & DSA_INDEX_TOPK_SCORE_ONLY)) return st;
+  }
+  // the rows' counts: q_pos + 1, else the sequence lengths (query i is then
+  // the last token of sequence i); the index kernel scored 0 .. count - 1
+  const int32_t* counts = q_pos ? q_pos : cache->seq_lens;
+  const int count_add = q_pos ? 1 : 0;
+  const GroupMaxIn gm{ws.m1, ws.m2, ws.ldg, ws.tau, (flags & DSA_TOPK_SEED_PREVIOUS) ? 1 : 0};
+  const int64_t per_thread = (ws.ldg + kFusedThreads - 1) / kFusedThreads;
+#define DSA_FUSED(RGV)                                                                         \
+  hipLaunchKernelGGL(topk_fused_kernel<RGV>, dim3(n_q), dim3(kFusedThreads), 0, stream, scores, \
+                     ld, counts, count_add, K, gm, idx)
+  // group-maximum slots per thread: every row fits (ld <= 262144: at most
+  // 16 * 1024 groups)
+  if (per_thread <= 2) DSA_FUSED(2);
+  else if (per_thread <= 4) DSA_FUSED(4);
+  else if (per_thread <= 8) DSA_FUSED(8);
+  else DSA_FUSED(16);
+#undef DSA_FUSED
   return launch_status();
 }

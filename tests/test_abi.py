@@ -107,6 +107,37 @@ def test_topk_validation(L):
     assert f(FAKE, (1 << 24) + 1, 4, 8, FAKE, 0, FAKE, FAKE, 1 << 40, None) == 2   # ld bound
 
 
+def test_index_topk_validation(L):
+    f = L.dsa_index_topk_decode
+    ws = L.dsa_index_topk_decode_ws(2, 1 << 17, 2048)
+    assert ws >= 2 * (1 << 17) // 16 * 8                     # two group maxima per 16 positions
+    assert L.dsa_index_topk_decode_ws(2, 1 << 20, 2048) >= 2 * (1 << 20) * 8   # long rows
+    c = cache()
+
+    def call(c=c, q=FAKE, q_seq=None, q_pos=None, n_q=2, H=64, K=2048, sc=FAKE, ld=1 << 17,
+             idx=FAKE, flags=0, w=FAKE, ws_bytes=ws):
+        return f(ctypes.byref(c), q, FAKE, q_seq, q_pos, n_q, H, K, sc, ld, idx, flags, w,
+                 ws_bytes, None)
+
+    assert call() == 5                                       # well formed: no gfx950 here
+    assert call(q=None) == 1
+    assert call(idx=None) == 1
+    assert call(q_seq=FAKE) == 1
+    assert call(c=cache(seq_lens=None)) == 1
+    assert call(c=cache(seq_lens=None), q_seq=FAKE, q_pos=FAKE, n_q=5,
+                ws_bytes=L.dsa_index_topk_decode_ws(5, 1 << 17, 2048)) == 5
+    assert call(n_q=3) == 2
+    assert call(K=0) == 2 and call(K=2049) == 2
+    assert call(ld=(1 << 17) + 2) == 2                       # ld must be a multiple of 4
+    assert call(flags=8) == 2
+    assert call(flags=2 | 4) == 2                            # score-only and select-only
+    assert call(flags=1) == 5 and call(flags=2) == 5 and call(flags=4) == 5
+    assert call(H=32) == 3
+    assert call(sc=FAKE + 4) == 3
+    assert call(w=None) == 4
+    assert call(ws_bytes=ws - 1) == 4
+
+
 def test_attention_validation(L):
     dec = L.dsa_sparse_attn_decode
     pre = L.dsa_sparse_attn_prefill

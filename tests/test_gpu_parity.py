@@ -36,6 +36,14 @@ def check_decode(wl, sample_rows=None, rel=False):
         np.testing.assert_array_equal(g_sc[b, :L], sc[b, :L], err_msg=f"scores row {b}")
     np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
     mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name, rel=rel)
+    # the separate index-score and Top-K calls give the same bits as the fused call
+    sep = dsa.DecodeStep(step.cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v,
+                         fused=False)
+    sep.select(dc.q_idx, dc.w)
+    torch.cuda.synchronize()
+    assert torch.equal(sep.idx, step.idx), "separate calls differ from the fused call"
+    for b, L in enumerate(wl.seq_lens):
+        assert torch.equal(sep.scores[b, :L], step.scores[b, :L])
     # attention alone, fed the oracle's indices
     o2, l2 = dsa.sparse_attn_decode(step.cache, dc.q, torch.from_numpy(idx).cuda(), wl.sm_scale)
     assert_attention(o2, l2, out, lse, wl.name + " (oracle idx)", rel=rel)
@@ -493,3 +501,186 @@ def test_debug_build_flags_bad_device_data():
     dsa.index_score(cache_len, dc.q_idx, dc.w, dsa.DSA_DECODE, out=st.scores, library=D)
     assert dsa.check_device_errors(library=D) == 7
     say("   ok: clean data passes, bad block / index / length are flagged")
+
+
+# ----------------------------------------------------------------------------- fused Top-K
+
+def _logical_rows(wl, bt, b, L):
+    return bt[b, np.arange(L) // wl.block_size] * wl.block_size + np.arange(L) % wl.block_size
+
+
+def _fused_case(wl, hc, what):
+    """Upload the host case's indexer keys / queries, run the fused and the
+    separate selection, compare both with the oracle bit for bit."""
+    say(f"[fused Top-K] {what}")
+    dc = dsa_synth.device_case(wl)
+    dc.k_idx.copy_(torch.from_numpy(hc.k_idx.view(np.int16)).view(torch.bfloat16)
+                   .reshape(dc.k_idx.shape))
+    dc.q_idx.copy_(torch.from_numpy(hc.q_idx.view(np.int16)).view(torch.bfloat16))
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    ld = max(wl.seq_lens)
+    fused = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, ld, wl.d_v)
+    sep = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, ld, wl.d_v, fused=False)
+    fused.select(dc.q_idx, dc.w)
+    sep.select(dc.q_idx, dc.w)
+    torch.cuda.synchronize()
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, hc.q_idx, hc.w, hc.q_seq,
+                            hc.q_pos, ld=ld)
+    idx = oracle.topk(sc, hc.q_pos + 1, wl.topk)
+    np.testing.assert_array_equal(fused.idx.cpu().numpy(), idx, err_msg=what)
+    np.testing.assert_array_equal(sep.idx.cpu().numpy(), idx, err_msg=what + " (separate)")
+    return fused
+
+
+def test_fused_topk_score_patterns():
+    """Score patterns chosen against the group-maxima bound: every score equal
+    (ties everywhere: the first K positions), scores constant within each
+    16-position group (group-level ties), the high scores packed into a few
+    groups, and a row whose top scores sit in the last, partial group."""
+    lens = [16385, 20000, 33000, 131072, 70001]
+    wl = dsa_synth.latent("fused_patterns", "decode", lens, seed=71, topk=2048, H_idx=64)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    bt = hc.block_table
+    one = 0x3F80  # bf16 1.0
+    # sequence 0: q = 0 -> every score 0
+    hc.q_idx[0] = 0
+    # sequence 1: key of position p is ((p // 16) % 3 - 1) in every column, q = 1
+    r = _logical_rows(wl, bt, 1, lens[1])
+    vals = np.array([0xBF80, 0x0000, 0x3F80], np.uint16)  # -1, 0, 1
+    hc.k_idx[r] = vals[(np.arange(lens[1]) // 16) % 3][:, None]
+    hc.q_idx[1] = one
+    # sequence 2: keys 0 except 3 groups of 16 with key 1 (plus random noise
+    # elsewhere below them): q = 1
+    r = _logical_rows(wl, bt, 2, lens[2])
+    hc.k_idx[r] = 0
+    for g in (5, 1000, 2062):
+        hc.k_idx[r[16 * g:16 * g + 16]] = one
+    hc.q_idx[2] = one
+    # sequence 4: the largest keys in the last (partial) group
+    r = _logical_rows(wl, bt, 4, lens[4])
+    hc.k_idx[r[-1:]] = 0x4040  # 3.0
+    hc.q_idx[4] = one
+    _fused_case(wl, hc, "patterns")
+
+
+def test_fused_topk_small_K():
+    # K = 37: rows have at least 4 K groups, the bound comes from the group
+    # maxima alone; the longest row uses every group slot of the kernel
+    wl = dsa_synth.latent("fused_smallK", "decode", [17000, 100000, 262144], seed=72, topk=37)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    _fused_case(wl, hc, "K=37, rows up to 262144")
+
+
+def test_index_topk_long_rows_with_query_positions():
+    """Row capacity past 262144: the fused call takes the long-row selection;
+    queries given by per-query positions (two per sequence, the second a few
+    positions before the end)."""
+    wl = dsa_synth.latent("long_rows_q", "decode", [20000, 300000, 1100000], seed=74, topk=2048)
+    say(f"[index + Top-K, long rows, per-query positions] {wl.seq_lens}")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    q_seq = np.repeat(np.arange(wl.n_seq, dtype=np.int32), 2)
+    q_pos = np.array([L - 1 - 5 * j for L in wl.seq_lens for j in range(2)], np.int32)
+    T = len(q_seq)
+    _, q_idx, w = dsa_synth.host_query_rows(wl, 0, T)
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    ld = (max(wl.seq_lens) + 63) // 64 * 64
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+    ws = dsa.index_topk_workspace(T, ld, wl.topk)
+    dsa.index_topk_decode(cache, _dev_bf16(q_idx), torch.from_numpy(w).cuda(), wl.topk, scores,
+                          idx, ws, q_seq=torch.from_numpy(q_seq).cuda(),
+                          q_pos=torch.from_numpy(q_pos).cuda())
+    torch.cuda.synchronize()
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos, ld=ld)
+    want = oracle.topk(sc, q_pos + 1, wl.topk)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+    say("   ok: Top-K exact")
+
+
+def test_fused_topk_with_query_positions():
+    # the fused selection with per-query positions (counts = q_pos + 1)
+    wl = dsa_synth.latent("fused_q", "decode", [30000, 90000], seed=75, topk=2048)
+    say(f"[fused index + Top-K, per-query positions] {wl.seq_lens}")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    q_seq = np.array([0, 0, 1, 1, 1], np.int32)
+    q_pos = np.array([29999, 17000, 89999, 45000, 16500], np.int32)
+    T = len(q_seq)
+    _, q_idx, w = dsa_synth.host_query_rows(wl, 0, T)
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
+    ld = 90048
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+    ws = dsa.index_topk_workspace(T, ld, wl.topk)
+    dsa.index_topk_decode(cache, _dev_bf16(q_idx), torch.from_numpy(w).cuda(), wl.topk, scores,
+                          idx, ws, q_seq=torch.from_numpy(q_seq).cuda(),
+                          q_pos=torch.from_numpy(q_pos).cuda())
+    torch.cuda.synchronize()
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos, ld=ld)
+    want = oracle.topk(sc, q_pos + 1, wl.topk)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+    say("   ok: Top-K exact")
+
+
+def test_incremental_decode_eight_steps():
+    """Eight consecutive decode steps: each appends one token per sequence
+    with dsa_cache_write, then runs the fused index score + Top-K with the
+    previous step's per-row threshold as a hint, and attention; every step
+    is compared with the oracle on the grown cache (indices bit-exact,
+    attention within the bars).  Queries drift slowly from step to step, as
+    consecutive decode queries do, so the hint is often usable."""
+    wl0 = dsa_synth.latent("incremental", "decode", [5000, 20000, 40000], seed=73, topk=2048)
+    steps = 8
+    # a cache with room for the appended tokens: the workload of the final
+    # lengths; the first steps see shorter sequences (seq_lens grows)
+    wl = dsa_synth.latent("incremental", "decode", [L + steps for L in wl0.seq_lens], seed=73,
+                          topk=2048)
+    say(f"[incremental decode] {wl0.seq_lens} + {steps} steps")
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    rng = np.random.default_rng(73)
+    lens = np.array(wl0.seq_lens, np.int32)
+    # the pool rows of the appended positions hold other values until written
+    for b, L in enumerate(lens):
+        rows = _logical_rows(wl, hc.block_table, b, L + steps)[L:]
+        hc.kv[rows] = 0
+        hc.k_idx[rows] = 0
+    dc.kv.view(-1, wl.d_qk)[torch.from_numpy(np.concatenate(
+        [_logical_rows(wl, hc.block_table, b, L + steps)[L:] for b, L in enumerate(lens)])).long()
+        .cuda()] = 0
+    seq_lens = torch.from_numpy(lens.copy()).cuda()
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, seq_lens, d_v=wl.d_v)
+    st = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, max(wl.seq_lens), wl.d_v,
+                        seed=True)
+    q_idx = hc.q_idx.copy()
+    for s_ in range(steps):
+        # append one token per sequence at position lens[b]
+        new_kv = _bf16_rows(rng, wl.n_q, wl.d_qk)
+        new_ki = rng.integers(-3, 4, (wl.n_q, wl.d_idx)).astype(np.float32)
+        new_ki = torch.from_numpy(new_ki).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        seq = np.arange(wl.n_q, dtype=np.int32)
+        pos = lens.copy()
+        dsa.cache_write(cache, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                        _dev_bf16(new_kv), _dev_bf16(new_ki))
+        oracle.cache_write(hc.kv, hc.block_table, wl.block_size, seq, pos, new_kv)
+        oracle.cache_write(hc.k_idx, hc.block_table, wl.block_size, seq, pos, new_ki)
+        lens += 1
+        seq_lens.copy_(torch.from_numpy(lens))
+        # the query drifts: a few indexer entries change per step
+        flip = rng.random(q_idx.shape) < 0.02
+        q_idx[flip] = torch.from_numpy(rng.integers(-3, 4, flip.sum()).astype(np.float32)).to(
+            torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        q = hc.q
+        st(_dev_bf16(q), _dev_bf16(q_idx), dc.w, wl.sm_scale)
+        torch.cuda.synchronize()
+        ld = int(lens.max())
+        sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, hc.w,
+                                np.arange(wl.n_q, dtype=np.int32), lens - 1, ld=ld)
+        idx = oracle.topk(sc, lens, wl.topk)
+        out, lse = oracle.sparse_attn(hc.kv, None, hc.block_table, wl.block_size, q,
+                                      np.arange(wl.n_q, dtype=np.int32), idx, wl.sm_scale,
+                                      d_v=wl.d_v)
+        np.testing.assert_array_equal(st.idx.cpu().numpy(), idx, err_msg=f"step {s_}")
+        mx, mn = assert_attention(st.out, st.lse, out, lse, f"step {s_}")
+        say(f"   step {s_}: lengths {lens.tolist()}: Top-K exact, attention max|err| {mx:.2e}")
