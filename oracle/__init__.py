@@ -25,12 +25,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # mutation check of the pins builds deliberately broken copies)
 LIB_PATH = os.environ.get("DSA_ORACLE_LIB") or os.path.join(_HERE, "libdsa_oracle.so")
 _lib = None
+SOURCES = ["dsa_oracle.c", "moe_oracle.c"]
 
 
 def build(verbose: bool = False) -> str:
     """Compile the oracle (gcc -O2 -fopenmp)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
-           os.path.join(_HERE, "dsa_oracle.c"), "-o", LIB_PATH + ".tmp", "-lm"]
+           *[os.path.join(_HERE, f) for f in SOURCES], "-o", LIB_PATH + ".tmp", "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("building the oracle failed:\n" + r.stderr)
@@ -55,6 +56,19 @@ def _load():
         L.oracle_sparse_attn.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32,
                                          i32, i32, dbl, vp, vp]
         L.oracle_sparse_attn.restype = None
+        u8 = ctypes.c_uint8
+        L.oracle_fp4_value.argtypes = [u8]
+        L.oracle_fp4_value.restype = dbl
+        L.oracle_e8m0_value.argtypes = [u8]
+        L.oracle_e8m0_value.restype = dbl
+        L.oracle_e4m3_value.argtypes = [u8]
+        L.oracle_e4m3_value.restype = dbl
+        L.oracle_e4m3_encode.argtypes = [dbl]
+        L.oracle_e4m3_encode.restype = u8
+        L.oracle_mxfp4_to_fp8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.oracle_mxfp4_to_fp8.restype = None
+        L.oracle_moe_gemm.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, vp, vp]
+        L.oracle_moe_gemm.restype = None
         _lib = L
     return _lib
 
@@ -168,3 +182,56 @@ def decode_step(case, K=None):
     out, lse = sparse_attn(case.kv, case.v, case.block_table, wl.block_size, case.q, case.q_seq,
                            idx, wl.sm_scale, d_v=wl.d_v)
     return sc, idx, out, lse
+
+
+# ----------------------------------------------------------------------------- MoE experts
+# (web pages "Day-0 Adaptation of Trillion-Parameter MoE Models on Domestic
+# GPUs", section 4; "Technical Path for Day-0 Adaptation of Trillion-Parameter
+# Models on Domestic GPUs", section 3.2: MXFP4 expert weights converted to FP8
+# just before the expert matrix product)
+
+def fp4_value(code: int) -> float:
+    """FP4 E2M1 code (0..15) -> value."""
+    return _load().oracle_fp4_value(code)
+
+
+def e8m0_value(code: int) -> float:
+    """E8M0 scale code -> 2^(code-127) (NaN for 255)."""
+    return _load().oracle_e8m0_value(code)
+
+
+def e4m3_value(code: int) -> float:
+    """FP8 E4M3 (OCP E4M3FN) code -> value."""
+    return _load().oracle_e4m3_value(code)
+
+
+def e4m3_encode(x: float) -> int:
+    """Real -> E4M3 code: round to nearest even, saturate at +-448."""
+    return _load().oracle_e4m3_encode(float(x))
+
+
+def mxfp4_to_fp8(codes, scales, expert_ids, N, K):
+    """E4M3 codes [E, N, K] of the listed experts' MXFP4 weights
+    (codes [experts, N, K/2] uint8, scales [experts, N, K/32] uint8)."""
+    c, c_p = _c(codes, np.uint8)
+    s_, s_p = _c(scales, np.uint8)
+    ids, ids_p = _c(expert_ids, np.int32)
+    out = np.empty((len(ids), N, K), dtype=np.uint8)
+    _load().oracle_mxfp4_to_fp8(c_p, s_p, ids_p, len(ids), N, K, out.ctypes.data)
+    return out
+
+
+def moe_gemm(x, row_offsets, expert_ids, codes, scales, N, K):
+    """y[r, n] = sum_k x[r, k] w8[n, k] for the rows of each listed expert
+    (x: E4M3 codes [M, K] uint8; row_offsets [E+1]).  fp32 [M, N]."""
+    x_, x_p = _c(x, np.uint8)
+    ro, ro_p = _c(row_offsets, np.int32)
+    ids, ids_p = _c(expert_ids, np.int32)
+    c, c_p = _c(codes, np.uint8)
+    s_, s_p = _c(scales, np.uint8)
+    M = x_.shape[0]
+    y = np.zeros((M, N), dtype=np.float32)
+    w8 = np.empty((N, K), dtype=np.uint8)
+    _load().oracle_moe_gemm(x_p, ro_p, ids_p, len(ids), c_p, s_p, N, K, w8.ctypes.data,
+                            y.ctypes.data)
+    return y
