@@ -12,6 +12,12 @@ The C ABI is declared in include/dsa.h; the names here match it:
   sparse_attn_prefill-> dsa_sparse_attn_prefill
   cache_write        -> dsa_cache_write
   check_device_errors-> dsa_check_device_errors
+and the MoE expert calls of include/dsa_moe.h:
+  moe_gemm_mxfp4     -> dsa_moe_gemm_mxfp4
+  mxfp4_to_fp8       -> dsa_mxfp4_to_fp8
+  moe_gemm_fp8       -> dsa_moe_gemm_fp8
+  moe_gemm_staged    -> dsa_moe_gemm_staged (MoeStaged holds its workspace,
+                        second stream and events)
 """
 from __future__ import annotations
 
@@ -26,7 +32,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 # the host cannot see (block-table entries, lengths, positions, kept indices)
 DEBUG_LIB_PATH = os.path.join(_HERE, "libdsa_debug.so")
 SOURCES = ["index_score.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_latent.hip",
-           "cache_write.hip"]
+           "cache_write.hip", "moe.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # keep packed-fp32 instructions out of the generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -94,6 +100,12 @@ def build_probe(verbose: bool = False) -> str:
     return PROBE_LIB
 
 
+class Mxfp4Weights(ctypes.Structure):
+    """Mirror of dsa_mxfp4_weights_t."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("num_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+
+
 class PagedCache(ctypes.Structure):
     """Mirror of dsa_paged_cache_t."""
     _fields_ = [("kv", ctypes.c_void_p), ("kv_row_stride", ctypes.c_int64),
@@ -130,11 +142,19 @@ def _configure(L):
     L.dsa_sparse_attn_prefill.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp]
     L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
     L.dsa_check_device_errors.argtypes = [vp]
+    pw = ctypes.POINTER(Mxfp4Weights)
+    L.dsa_moe_gemm_mxfp4.argtypes = [pw, vp, vp, vp, i32, i32, i32, vp, vp]
+    L.dsa_mxfp4_to_fp8.argtypes = [pw, vp, i32, vp, vp]
+    L.dsa_moe_gemm_fp8.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, vp, vp]
+    L.dsa_moe_staged_ws.argtypes = [i32, i32, i32]
+    L.dsa_moe_staged_ws.restype = sz
+    L.dsa_moe_gemm_staged.argtypes = [pw, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp]
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
     for f in (L.dsa_index_score, L.dsa_topk, L.dsa_index_topk_decode, L.dsa_sparse_attn_decode,
               L.dsa_sparse_attn_decode_static, L.dsa_sparse_attn_prefill, L.dsa_cache_write,
-              L.dsa_check_device_errors):
+              L.dsa_check_device_errors, L.dsa_moe_gemm_mxfp4, L.dsa_mxfp4_to_fp8,
+              L.dsa_moe_gemm_fp8, L.dsa_moe_gemm_staged):
         f.restype = i32
     return L
 
@@ -489,3 +509,148 @@ class PrefillStep:
         sparse_attn_prefill(c, q, self.q_seq, self.q_pos, self.idx, sm_scale, out=self.out,
                             lse=self.lse, stream=stream, library=library)
         return self.out, self.lse
+
+
+class Experts:
+    """One layer's MXFP4 expert weights in device memory (referenced, not
+    copied): codes uint8 [num_experts, N, K/2] (element 2i in the low
+    nibble), scales uint8 [num_experts, N, K/32] (E8M0)."""
+
+    def __init__(self, codes, scales):
+        import torch
+
+        _need(codes, torch.uint8, "codes")
+        _need(scales, torch.uint8, "scales")
+        E, N, K2 = codes.shape
+        if scales.shape != (E, N, 2 * K2 // 32):
+            raise ValueError(f"scales must be [{E}, {N}, {2 * K2 // 32}], got {tuple(scales.shape)}")
+        self.tensors = (codes, scales)
+        self.w = Mxfp4Weights(codes.data_ptr(), scales.data_ptr(), E, N, 2 * K2)
+
+    @property
+    def N(self):
+        return self.w.N
+
+    @property
+    def K(self):
+        return self.w.K
+
+
+def _routing(x, expert_ids, row_offsets):
+    import torch
+
+    _need(x, torch.uint8, "x")
+    _need(row_offsets, torch.int32, "row_offsets")
+    if expert_ids is not None:
+        _need(expert_ids, torch.int32, "expert_ids")
+    return row_offsets.shape[0] - 1, x.shape[0]
+
+
+def moe_gemm_mxfp4(experts: Experts, x, expert_ids, row_offsets, max_rows: int, out=None,
+                   stream=None, library=None):
+    """dsa_moe_gemm_mxfp4: fp32 y [M, N] = x (E4M3 codes [M, K]) times the
+    routed experts' weights, converted to E4M3 in registers."""
+    import torch
+
+    L = library or lib()
+    n_act, M = _routing(x, expert_ids, row_offsets)
+    if out is None:
+        out = torch.empty((M, experts.N), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "y")
+    _check(L.dsa_moe_gemm_mxfp4(ctypes.byref(experts.w), x.data_ptr(), expert_ids.data_ptr(),
+                                row_offsets.data_ptr(), n_act, M, max_rows, out.data_ptr(),
+                                _stream(stream)), "dsa_moe_gemm_mxfp4", L)
+    return out
+
+
+def mxfp4_to_fp8(experts: Experts, expert_ids, out=None, stream=None, library=None):
+    """dsa_mxfp4_to_fp8: uint8 E4M3 codes [n_act, N, K] of the listed experts."""
+    import torch
+
+    L = library or lib()
+    _need(expert_ids, torch.int32, "expert_ids")
+    n_act = expert_ids.shape[0]
+    if out is None:
+        out = torch.empty((n_act, experts.N, experts.K), dtype=torch.uint8,
+                          device=expert_ids.device)
+    _need(out, torch.uint8, "w8")
+    _check(L.dsa_mxfp4_to_fp8(ctypes.byref(experts.w), expert_ids.data_ptr(), n_act,
+                              out.data_ptr(), _stream(stream)), "dsa_mxfp4_to_fp8", L)
+    return out
+
+
+def moe_gemm_fp8(w8, x, row_offsets, max_rows: int, out=None, stream=None, library=None):
+    """dsa_moe_gemm_fp8: fp32 y [M, N] from converted weights w8 [n_act, N, K]."""
+    import torch
+
+    L = library or lib()
+    _need(w8, torch.uint8, "w8")
+    n_act, M = _routing(x, None, row_offsets)
+    _, N, K = w8.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "y")
+    _check(L.dsa_moe_gemm_fp8(w8.data_ptr(), N, K, x.data_ptr(), row_offsets.data_ptr(), n_act,
+                              M, max_rows, out.data_ptr(), _stream(stream)), "dsa_moe_gemm_fp8", L)
+    return out
+
+
+_hip = None
+
+
+def _hip_runtime():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return _hip
+
+
+class MoeStaged:
+    """The staged expert pipeline's state that every layer shares: one FP8
+    workspace of two halves (chunk_experts experts each), a second stream
+    for the conversions and the four events that order the halves' reuse
+    (dsa_moe_gemm_staged).  Call it once per layer, in layer order."""
+
+    def __init__(self, N: int, K: int, chunk_experts: int, device="cuda"):
+        import torch
+
+        n = lib().dsa_moe_staged_ws(N, K, chunk_experts)
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        self.conv_stream = torch.cuda.Stream(device=device)
+        H = _hip_runtime()
+        self._events = (ctypes.c_void_p * 4)()
+        for i in range(4):
+            ev = ctypes.c_void_p()
+            if H.hipEventCreateWithFlags(ctypes.byref(ev), 2) != 0:  # hipEventDisableTiming
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._events[i] = ev.value
+
+    def __call__(self, experts: Experts, x, expert_ids, row_offsets, max_rows: int, out=None,
+                 stream=None, library=None):
+        import torch
+
+        L = library or lib()
+        n_act, M = _routing(x, expert_ids, row_offsets)
+        if out is None:
+            out = torch.empty((M, experts.N), dtype=torch.float32, device=x.device)
+        _need(out, torch.float32, "y")
+        _check(L.dsa_moe_gemm_staged(ctypes.byref(experts.w), x.data_ptr(), expert_ids.data_ptr(),
+                                     row_offsets.data_ptr(), n_act, M, max_rows, out.data_ptr(),
+                                     self.workspace.data_ptr(), self.workspace.numel(),
+                                     _stream(stream), ctypes.c_void_p(self.conv_stream.cuda_stream),
+                                     self._events), "dsa_moe_gemm_staged", L)
+        return out
+
+    def __del__(self):
+        try:
+            import torch
+
+            torch.cuda.synchronize()
+            H = _hip_runtime()
+            for ev in self._events:
+                if ev:
+                    H.hipEventDestroy(ctypes.c_void_p(ev))
+        except Exception:
+            pass

@@ -44,6 +44,7 @@ inline dsa_status_t check_cache_common(const dsa_paged_cache_t* c) {
 __attribute__((visibility("hidden"))) uint32_t take_bounds_error_index_score(hipStream_t stream);
 __attribute__((visibility("hidden"))) uint32_t take_bounds_error_topk(hipStream_t stream);
 __attribute__((visibility("hidden"))) uint32_t take_bounds_error_cache_write(hipStream_t stream);
+__attribute__((visibility("hidden"))) uint32_t take_bounds_error_moe(hipStream_t stream);
 
 // The decode index score that also writes each 16-position group's two
 // largest scores (the fused index + Top-K call), in index_score.hip.

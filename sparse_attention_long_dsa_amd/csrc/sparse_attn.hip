@@ -515,7 +515,7 @@ extern "C" dsa_status_t dsa_check_device_errors(hipStream_t stream) {
   if (!kCheckBounds) return DSA_ERR_UNSUPPORTED;
   const uint32_t e = take_bounds_error_small(stream) | take_bounds_error_latent(stream) |
                      take_bounds_error_index_score(stream) | take_bounds_error_topk(stream) |
-                     take_bounds_error_cache_write(stream);
+                     take_bounds_error_cache_write(stream) | take_bounds_error_moe(stream);
   if (e & 0x80000000u) return DSA_ERR_HIP;
   return e ? DSA_ERR_BOUNDS : DSA_OK;
 }

@@ -1,5 +1,5 @@
 """The C ABI without a GPU: libdsa.so loads, exports every function that
-include/dsa.h declares, and rejects bad arguments on the host before any
+include/dsa.h and include/dsa_moe.h declare, and rejects bad arguments on the host before any
 launch (on a machine with no GPU, well-formed calls stop at the device check)."""
 import ctypes
 import os
@@ -10,13 +10,15 @@ import pytest
 import sparse_attention_long_dsa_amd as dsa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dsa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("dsa.h", "dsa_moe.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dsa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,9 +28,11 @@ def L():
     return dsa.lib()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_attn_decode", "dsa_sparse_attn_prefill"):
+    for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_attn_decode", "dsa_sparse_attn_prefill",
+              "dsa_moe_gemm_mxfp4", "dsa_mxfp4_to_fp8", "dsa_moe_gemm_fp8",
+              "dsa_moe_gemm_staged"):
         assert f in names
 
 
@@ -227,3 +231,54 @@ def test_cache_write_validation(L):
     assert f(ctypes.byref(cache(d_qk=570, kv_row_stride=576)), FAKE, FAKE, 4, FAKE, None, FAKE,
              None) == 3
     assert f(ctypes.byref(c), FAKE, FAKE, 4, FAKE + 8, None, FAKE, None) == 3  # alignment
+
+
+def weights(**kw):
+    w = dict(codes=FAKE, scales=FAKE, num_experts=8, N=64, K=256)
+    w.update(kw)
+    return dsa.Mxfp4Weights(**w)
+
+
+def test_moe_validation(L):
+    f = L.dsa_moe_gemm_mxfp4
+    w = weights()
+
+    def gemm(w=w, x=FAKE, ids=FAKE, offs=FAKE, n_act=4, M=16, max_rows=4, y=FAKE):
+        return f(ctypes.byref(w) if w is not None else None, x, ids, offs, n_act, M, max_rows, y,
+                 None)
+
+    assert gemm() == 5                                  # well formed: stops at the device check
+    assert gemm(w=None) == 1
+    assert gemm(x=None) == 1 and gemm(ids=None) == 1 and gemm(offs=None) == 1 and gemm(y=None) == 1
+    assert gemm(w=weights(codes=None)) == 1
+    assert gemm(n_act=0) == 2 and gemm(n_act=65536) == 2 and gemm(M=-1) == 2
+    assert gemm(w=weights(num_experts=0)) == 2
+    assert gemm(w=weights(K=200)) == 3                  # K not a multiple of 128
+    assert gemm(w=weights(N=40)) == 3                   # N not a multiple of 16
+    assert gemm(x=FAKE + 8) == 3 and gemm(w=weights(codes=FAKE + 4)) == 3
+    assert gemm(w=weights(scales=FAKE + 2)) == 3
+    c = L.dsa_mxfp4_to_fp8
+    assert c(ctypes.byref(w), FAKE, 4, FAKE, None) == 5
+    assert c(ctypes.byref(w), FAKE, 4, None, None) == 1
+    assert c(ctypes.byref(w), None, 4, FAKE, None) == 1
+    assert c(ctypes.byref(w), FAKE, 0, FAKE, None) == 2
+    g = L.dsa_moe_gemm_fp8
+    assert g(FAKE, 64, 256, FAKE, FAKE, 4, 16, 4, FAKE, None) == 5
+    assert g(None, 64, 256, FAKE, FAKE, 4, 16, 4, FAKE, None) == 1
+    assert g(FAKE, 64, 250, FAKE, FAKE, 4, 16, 4, FAKE, None) == 3
+    assert g(FAKE, 0, 256, FAKE, FAKE, 4, 16, 4, FAKE, None) == 2
+    assert L.dsa_moe_staged_ws(64, 256, 3) == 2 * 3 * 64 * 256
+    assert L.dsa_moe_staged_ws(64, 256, 0) == 0
+    s = L.dsa_moe_gemm_staged
+    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    ws = L.dsa_moe_staged_ws(64, 256, 1)
+
+    def staged(ws_bytes=ws, stream=None, conv=FAKE, events=ev):
+        return s(ctypes.byref(w), FAKE, FAKE, FAKE, 4, 16, 4, FAKE, FAKE, ws_bytes, stream, conv,
+                 events)
+
+    assert staged() == 5
+    assert staged(ws_bytes=ws - 1) == 4                 # not even one expert a half
+    assert staged(events=None) == 1
+    assert staged(events=(ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)) == 1
+    assert staged(conv=None) == 2                       # conversion stream == product stream
