@@ -10,7 +10,7 @@ Recipes:
   * weight codes: uniform random bytes (every FP4 code, both nibbles);
   * scales: E8M0 codes uniform on [scale_lo, scale_hi]; 126..128 (2^-1 ..
     2^1) keeps every product sum exact in fp32 for K <= 8192 with integer
-    tokens, 122..133 is the range where the FP8 conversion is exact, and
+    tokens, 119..133 is the range where the FP8 conversion is exact, and
     wider ranges reach the FP8 subnormals and the saturation;
   * tokens: "int" -> integers uniform on [-4, 4]; "normal" -> N(0, 1) cast to
     E4M3;

@@ -13,7 +13,8 @@
  * kept.  Three ways to run it:
  *   - dsa_moe_gemm_mxfp4: the conversion happens in registers inside the
  *     product kernel (the weights are read once, at 4.25 bits an element);
- *     no workspace at all;
+ *     no workspace at all; fastest on weights packed once, at load time,
+ *     into the tiled layout (dsa_mxfp4_pack);
  *   - dsa_mxfp4_to_fp8 + dsa_moe_gemm_fp8: conversion into a caller's FP8
  *     workspace, then the product from it;
  *   - dsa_moe_gemm_staged: the pages' pipeline -- chunks of the listed
@@ -24,15 +25,24 @@
  * All three compute the same values.
  *
  * Formats (OCP Microscaling Formats (MX) v1.0):
- *   - weights of one layer: codes uint8 [num_experts, N, K/2], two FP4 E2M1
- *     elements a byte (element 2i of a row in the low nibble, 2i+1 in the
- *     high nibble), and scales uint8 [num_experts, N, K/32], one E8M0 scale
- *     (2^(code-127); code 255 is NaN) for each 32 consecutive elements of a
- *     row;
+ *   - weights of one layer, DSA_MXFP4_ROW_MAJOR: codes uint8 [num_experts,
+ *     N, K/2], two FP4 E2M1 elements a byte (element 2i of a row in the low
+ *     nibble, 2i+1 in the high nibble), and scales uint8 [num_experts, N,
+ *     K/32], one E8M0 scale (2^(code-127); code 255 is NaN) for each 32
+ *     consecutive elements (an MX block) of a row;
+ *   - DSA_MXFP4_TILED (K a multiple of 256): the same bytes reordered so
+ *     that what one 64-lane wave loads is contiguous.  Each expert's rows
+ *     are cut into tiles of 16 (tile t = n / 16, r = n % 16) and each row
+ *     into units of 256 elements (u = k / 256); unit (t, u) of expert e
+ *     holds 2048 code bytes at ((e * N/16 + t) * K/256 + u) * 2048 and 128
+ *     scale bytes at the same unit index * 128.  Inside a unit, MX block
+ *     b = (k % 256) / 32 of row r belongs to lane L = 16 * (b / 2) + r and
+ *     half h = b % 2: its 16 code bytes (same nibble order) sit at byte
+ *     1024 h + 16 L and its scale at byte 2 L + h;
  *   - FP8 is E4M3 (the OCP "E4M3FN" encoding: bias 7, largest finite 448,
  *     S.1111.111 NaN).  The converted weight is the E4M3 number nearest to
  *     scale x element (ties to even mantissa), saturated to +-448 (a NaN
- *     scale gives 0x7f); the conversion is exact for scale codes 122..133;
+ *     scale gives 0x7f); the conversion is exact for scale codes 119..133;
  *   - the routed tokens x are E4M3 codes [M, K]; the result y is fp32
  *     [M, N]: y[r, n] = sum_k x[r, k] * w8_e[n, k] with the products exact
  *     and the sum accumulated in fp32 on the matrix cores.
@@ -66,14 +76,25 @@
 extern "C" {
 #endif
 
+#define DSA_MXFP4_ROW_MAJOR 0
+#define DSA_MXFP4_TILED 1
+
 /* One layer's MXFP4 expert weights (device pointers). */
 typedef struct {
-  const uint8_t *codes;   /* [num_experts, N, K/2] FP4 E2M1 pairs */
-  const uint8_t *scales;  /* [num_experts, N, K/32] E8M0          */
+  const uint8_t *codes;   /* num_experts * N * K/2 FP4 E2M1 pairs  */
+  const uint8_t *scales;  /* num_experts * N * K/32 E8M0 (4-byte aligned) */
   int32_t num_experts;
-  int32_t N;              /* output features of each expert       */
-  int32_t K;              /* input features                       */
+  int32_t N;              /* output features of each expert        */
+  int32_t K;              /* input features                        */
+  int32_t layout;         /* DSA_MXFP4_ROW_MAJOR or DSA_MXFP4_TILED */
 } dsa_mxfp4_weights_t;
+
+/* Reorders row-major weights (w->layout == DSA_MXFP4_ROW_MAJOR, K a
+ * multiple of 256) into the tiled layout: codes_tiled and scales_tiled
+ * receive the same number of bytes as w's arrays (no value changes; done
+ * once when the weights are loaded).  DSA_ERR_SHAPE for tiled input. */
+dsa_status_t dsa_mxfp4_pack(const dsa_mxfp4_weights_t *w, uint8_t *codes_tiled,
+                            uint8_t *scales_tiled, hipStream_t stream);
 
 /* Expert product with the MXFP4 -> FP8 conversion done in registers inside
  * the product kernel (page 2, section 3.2: conversion and product
@@ -84,8 +105,8 @@ dsa_status_t dsa_moe_gemm_mxfp4(const dsa_mxfp4_weights_t *w, const uint8_t *x,
                                 hipStream_t stream);
 
 /* The conversion on its own (page 1, section 4: dequantise to 8-bit right
- * before the product): w8[i] ([n_act, N, K] E4M3 bytes) receives the
- * converted weights of expert expert_ids[i]. */
+ * before the product): w8[i] ([n_act, N, K] E4M3 bytes, row-major whatever
+ * w's layout) receives the converted weights of expert expert_ids[i]. */
 dsa_status_t dsa_mxfp4_to_fp8(const dsa_mxfp4_weights_t *w, const int32_t *expert_ids,
                               int32_t n_act, uint8_t *w8, hipStream_t stream);
 
@@ -105,18 +126,22 @@ size_t dsa_moe_staged_ws(int32_t N, int32_t K, int32_t chunk_experts);
  * chunks of chunk = workspace_bytes / (2 N K) experts (at least 1, else
  * DSA_ERR_WORKSPACE); chunk c is converted on conv_stream into half c % 2
  * of the workspace and multiplied on `stream`.  Ordering, all by events:
+ *   - at entry the call records events[4] on `stream` and conv_stream waits
+ *     for it, so the conversions see everything enqueued on `stream` before
+ *     the call (weights written there, the workspace's earlier users);
  *   - conversion c waits for events[2 + c % 2] ("half free"), recorded on
  *     `stream` after the product that last read that half -- in this call
  *     or an earlier one: the same workspace and events serve every layer;
  *   - product c waits for events[c % 2] ("half converted"), recorded on
  *     conv_stream after conversion c.
- * events: four caller-owned events (created with hipEventDisableTiming
+ * events: five caller-owned events (created with hipEventDisableTiming
  * preferably) that stay with this workspace for its lifetime; events never
- * recorded before count as complete.  conv_stream must differ from
- * `stream`.  When the call returns, everything is enqueued; y is complete
- * once `stream` has reached its end (the conversions all precede products
- * on it).  The caller must not touch the workspace until then.  Results
- * equal dsa_moe_gemm_mxfp4's. */
+ * recorded before count as complete.  With K a multiple of 256 the
+ * workspace holds the converted weights in the tiled unit order (4096
+ * bytes a unit).  conv_stream must differ from `stream`.  When the call
+ * returns, everything is enqueued; y is complete once `stream` has reached
+ * its end (every conversion precedes a product on it).  Results equal
+ * dsa_moe_gemm_mxfp4's. */
 dsa_status_t dsa_moe_gemm_staged(const dsa_mxfp4_weights_t *w, const uint8_t *x,
                                  const int32_t *expert_ids, const int32_t *row_offsets,
                                  int32_t n_act, int32_t M, int32_t max_rows, float *y,

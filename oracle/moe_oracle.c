@@ -26,7 +26,8 @@
  *     saturates at +-448 ("satfinite").
  * Readings taken where the pages are silent: the conversion applies the
  * block scale (the FP8 weight equals scale x element, exactly so whenever
- * that value is an E4M3 number), the routed tokens are FP8 E4M3 as well (an
+ * that value is an E4M3 number, which holds for every element when the
+ * scale code is in 119..133), the routed tokens are FP8 E4M3 as well (an
  * "8-bit matrix multiply"), and the product accumulates in double here and
  * is stored as fp32.
  */

@@ -38,6 +38,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 DSA_PREFILL, DSA_DECODE = 0, 1
+DSA_MXFP4_ROW_MAJOR, DSA_MXFP4_TILED = 0, 1
 DSA_TOPK_SEED_PREVIOUS, DSA_INDEX_TOPK_SCORE_ONLY, DSA_INDEX_TOPK_SELECT_ONLY = 1, 2, 4
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
           4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_DEVICE", 6: "DSA_ERR_HIP", 7: "DSA_ERR_BOUNDS"}
@@ -103,7 +104,8 @@ def build_probe(verbose: bool = False) -> str:
 class Mxfp4Weights(ctypes.Structure):
     """Mirror of dsa_mxfp4_weights_t."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("num_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+                ("num_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class PagedCache(ctypes.Structure):
@@ -143,6 +145,7 @@ def _configure(L):
     L.dsa_cache_write.argtypes = [pc, vp, vp, i32, vp, vp, vp, vp]
     L.dsa_check_device_errors.argtypes = [vp]
     pw = ctypes.POINTER(Mxfp4Weights)
+    L.dsa_mxfp4_pack.argtypes = [pw, vp, vp, vp]
     L.dsa_moe_gemm_mxfp4.argtypes = [pw, vp, vp, vp, i32, i32, i32, vp, vp]
     L.dsa_mxfp4_to_fp8.argtypes = [pw, vp, i32, vp, vp]
     L.dsa_moe_gemm_fp8.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, vp, vp]
@@ -153,7 +156,7 @@ def _configure(L):
     L.dsa_status_string.restype = ctypes.c_char_p
     for f in (L.dsa_index_score, L.dsa_topk, L.dsa_index_topk_decode, L.dsa_sparse_attn_decode,
               L.dsa_sparse_attn_decode_static, L.dsa_sparse_attn_prefill, L.dsa_cache_write,
-              L.dsa_check_device_errors, L.dsa_moe_gemm_mxfp4, L.dsa_mxfp4_to_fp8,
+              L.dsa_check_device_errors, L.dsa_mxfp4_pack, L.dsa_moe_gemm_mxfp4, L.dsa_mxfp4_to_fp8,
               L.dsa_moe_gemm_fp8, L.dsa_moe_gemm_staged):
         f.restype = i32
     return L
@@ -514,9 +517,10 @@ class PrefillStep:
 class Experts:
     """One layer's MXFP4 expert weights in device memory (referenced, not
     copied): codes uint8 [num_experts, N, K/2] (element 2i in the low
-    nibble), scales uint8 [num_experts, N, K/32] (E8M0)."""
+    nibble), scales uint8 [num_experts, N, K/32] (E8M0), in row-major
+    (DSA_MXFP4_ROW_MAJOR) or tiled (DSA_MXFP4_TILED) byte order."""
 
-    def __init__(self, codes, scales):
+    def __init__(self, codes, scales, layout: int = DSA_MXFP4_ROW_MAJOR):
         import torch
 
         _need(codes, torch.uint8, "codes")
@@ -525,7 +529,7 @@ class Experts:
         if scales.shape != (E, N, 2 * K2 // 32):
             raise ValueError(f"scales must be [{E}, {N}, {2 * K2 // 32}], got {tuple(scales.shape)}")
         self.tensors = (codes, scales)
-        self.w = Mxfp4Weights(codes.data_ptr(), scales.data_ptr(), E, N, 2 * K2)
+        self.w = Mxfp4Weights(codes.data_ptr(), scales.data_ptr(), E, N, 2 * K2, layout)
 
     @property
     def N(self):
@@ -534,6 +538,17 @@ class Experts:
     @property
     def K(self):
         return self.w.K
+
+    def tiled(self, stream=None, library=None) -> "Experts":
+        """dsa_mxfp4_pack: a tiled copy of row-major weights."""
+        import torch
+
+        L = library or lib()
+        codes, scales = self.tensors
+        c2, s2 = torch.empty_like(codes), torch.empty_like(scales)
+        _check(L.dsa_mxfp4_pack(ctypes.byref(self.w), c2.data_ptr(), s2.data_ptr(),
+                                _stream(stream)), "dsa_mxfp4_pack", L)
+        return Experts(c2, s2, DSA_MXFP4_TILED)
 
 
 def _routing(x, expert_ids, row_offsets):
@@ -610,8 +625,9 @@ def _hip_runtime():
 class MoeStaged:
     """The staged expert pipeline's state that every layer shares: one FP8
     workspace of two halves (chunk_experts experts each), a second stream
-    for the conversions and the four events that order the halves' reuse
-    (dsa_moe_gemm_staged).  Call it once per layer, in layer order."""
+    for the conversions and the five events that order them against the
+    products and the halves' reuse (dsa_moe_gemm_staged).  Call it once per
+    layer, in layer order."""
 
     def __init__(self, N: int, K: int, chunk_experts: int, device="cuda"):
         import torch
@@ -620,8 +636,8 @@ class MoeStaged:
         self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
         self.conv_stream = torch.cuda.Stream(device=device)
         H = _hip_runtime()
-        self._events = (ctypes.c_void_p * 4)()
-        for i in range(4):
+        self._events = (ctypes.c_void_p * 5)()
+        for i in range(5):
             ev = ctypes.c_void_p()
             if H.hipEventCreateWithFlags(ctypes.byref(ev), 2) != 0:  # hipEventDisableTiming
                 raise RuntimeError("hipEventCreateWithFlags failed")

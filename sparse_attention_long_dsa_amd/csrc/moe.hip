@@ -14,9 +14,19 @@
 // bytes of the eight FP4 magnitudes (two dwords) and the sign mask, so the
 // magnitudes go through two v_perm_b32 lookups and the signs are OR-ed in.
 // Decode-sized expert batches (a few tokens an expert) are bound by
-// reading the weights from HBM: each wave streams its weight rows once, 64
-// bytes of codes a lane ahead of use, and reads the (few) token rows
-// through L2.
+// reading the weights from HBM: each wave streams its weight rows once, one
+// super-step ahead of use, and reads the (few) token rows through L2.
+//
+// Weight layouts.  Row-major MXFP4 ([E, N, K/2] codes) makes a wave's 16
+// rows 16 separate 128-byte pieces per super-step, which streams at about
+// half of HBM speed; the tiled layout (DSA_MXFP4_TILED, made once by
+// dsa_mxfp4_pack, still 4.25 bits an element) stores each 16-row x 256-k
+// unit as one 2 KB block in the order the lanes read it, so every wave load
+// is one contiguous KB.  The staged pipeline's FP8 workspace uses the same
+// unit order (4 KB a unit).  Lane (row r, group g) of a unit holds k =
+// 64 g .. 64 g + 63 as two MX blocks (one per 128-k step), in both layouts
+// and in both kernels, so every path sums the same products in the same
+// order and gives the same bits.
 #include "common.h"
 #include "host_util.h"
 
@@ -117,21 +127,50 @@ __device__ __forceinline__ void expert_rows(const int32_t* __restrict__ row_offs
   }
 }
 
+constexpr int kUnitK = 256;  // k elements of one tiled unit
+
+// Per-lane strides of the weight sources (bytes): a super-step advances by
+// kStep, the 16-byte pieces of one super-step lie kPiece apart; scales
+// advance by kScaleStep.
+template <bool kFp4, bool kTiled, int S>
+struct WeightStrides {
+  static constexpr int kStep = kTiled ? (kFp4 ? 2048 : 4096) : (kFp4 ? 64 * S : 128 * S);
+  static constexpr int kPiece = kTiled ? 1024 : 16;
+  static constexpr int kScaleStep = kTiled ? 128 : 4 * S;
+};
+
+// Byte offsets of (row n, 32-k block kb) of one expert's codes / scales in
+// a layout (the block's 16 code bytes are contiguous in both).
+__device__ __forceinline__ int64_t code_offset(bool tiled, int64_t n, int64_t kb, int N, int K) {
+  if (!tiled) return n * (K / 2) + 16 * kb;
+  const int64_t unit = (n / 16) * (K / kUnitK) + kb / 8;
+  const int lane = (int)((kb % 8) / 2) * 16 + (int)(n % 16);
+  return unit * 2048 + (kb % 2) * 1024 + lane * 16;
+}
+__device__ __forceinline__ int64_t scale_offset(bool tiled, int64_t n, int64_t kb, int N, int K) {
+  if (!tiled) return n * (K / 32) + kb;
+  const int64_t unit = (n / 16) * (K / kUnitK) + kb / 8;
+  const int lane = (int)((kb % 8) / 2) * 16 + (int)(n % 16);
+  return unit * 128 + lane * 2 + kb % 2;
+}
+
 // One super-step of a lane's weight bytes: kRaw 16-byte pieces of each of
-// its NT rows, and (MXFP4) the S scale bytes of each.
-template <int NT, int kRaw, int S, bool kFp4>
+// its NT rows, and (MXFP4) the S scale bytes of each.  Loads are
+// unconditional (rows past N read a clamped row), so the compiler's wait
+// counts stay exact: waiting for an older super-step never waits for these.
+template <int NT, int kRaw, int S, bool kFp4, bool kTiled>
 __device__ __forceinline__ void load_weights(u32x4 (&raw)[NT][kRaw], uint32_t (&sc)[NT],
                                              const uint8_t* const (&wrow)[NT],
-                                             const uint8_t* const (&srow)[NT],
-                                             const bool (&tile_ok)[NT], int step) {
+                                             const uint8_t* const (&srow)[NT], int step) {
+  using St = WeightStrides<kFp4, kTiled, S>;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    if (!tile_ok[j]) continue;
-    const u32x4* p = (const u32x4*)(wrow[j] + (int64_t)step * 64 * kRaw);  // 4 groups x 16 kRaw
+    const uint8_t* p = wrow[j] + (int64_t)step * St::kStep;
 #pragma unroll
-    for (int q = 0; q < kRaw; ++q) raw[j][q] = __builtin_nontemporal_load(p + q);
+    for (int q = 0; q < kRaw; ++q)
+      raw[j][q] = __builtin_nontemporal_load((const u32x4*)(p + q * St::kPiece));
     if constexpr (kFp4) {
-      const uint8_t* sp = srow[j] + (int64_t)step * 4 * S;
+      const uint8_t* sp = srow[j] + (int64_t)step * St::kScaleStep;
       if constexpr (S == 4) sc[j] = *(const uint32_t*)sp;
       else if constexpr (S == 2) sc[j] = *(const uint16_t*)sp;
       else sc[j] = *sp;
@@ -139,20 +178,64 @@ __device__ __forceinline__ void load_weights(u32x4 (&raw)[NT][kRaw], uint32_t (&
   }
 }
 
+// One super-step of a lane's token bytes: 32 S bytes of each of its RT rows
+// (rows past the expert's count read a clamped row).
+template <int RT, int S>
+__device__ __forceinline__ void load_tokens(u32x4 (&xa)[RT][2 * S],
+                                            const uint8_t* const (&xrow)[RT], int step) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const u32x4* p = (const u32x4*)(xrow[t] + (int64_t)step * 128 * S);
+#pragma unroll
+    for (int q = 0; q < 2 * S; ++q) xa[t][q] = p[q];
+  }
+}
+
+// The products of one super-step.
+template <int NT, int RT, int S, bool kFp4, int kRaw>
+__device__ __forceinline__ void super_step(f32x4 (&acc)[RT][NT], const u32x4 (&w)[NT][kRaw],
+                                           const uint32_t (&sc)[NT], const u32x4 (&xa)[RT][2 * S],
+                                           const ScaleEntry* tab) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    // Lanes of rows past the expert's count hold a clamped row: row i of the
+    // product depends on row i of the tokens only, and those rows are never
+    // stored.
+    i32x8 a[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) a[t] = join(xa[t][2 * s], xa[t][2 * s + 1]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      i32x8 b;
+      if constexpr (kFp4) {
+        b = convert_block(w[j][s], tab[(sc[j] >> (8 * s)) & 255]);
+      } else {
+        b = join(w[j][2 * s], w[j][2 * s + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t][j] = mfma_fp8(a[t], b, acc[t][j]);
+    }
+  }
+}
+
 // The product kernel.  Workgroup (b, i, z): listed expert i, weight rows
 // n0 = 64 NT b .. +64 NT (wave w takes NT tiles of 16 rows), token rows in
 // passes of 16 RT starting at pass z, stepping gridDim.z.  kFp4: weights
-// are MXFP4 codes + scales of expert expert_ids[i]; else E4M3 bytes w8[i].
+// are MXFP4 codes + scales of expert expert_ids[i]; else E4M3 bytes of
+// listed expert i.  kTiled: the weights are in unit order (then S = 2).
 // The k loop runs in super-steps of 128 S: lane (row l & 15, group g = l >>
-// 4) holds k = kk + 32 S g + 32 s .. +31 in step s, for the weights (16 S
-// code bytes, S scale bytes, loaded one super-step ahead) and the tokens
-// alike.
-template <int NT, int RT, int S, bool kFp4>
+// 4) holds k = kk + 32 S g + 32 s .. +31 in step s, for the weights and the
+// tokens alike.  Order of loads in a super-step: its token bytes, then the
+// next super-step's weights, then the products -- so the products wait for
+// nothing issued after the loads they use, and each wave keeps one
+// super-step of weights in flight.
+template <int NT, int RT, int S, bool kFp4, bool kTiled>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
     const uint8_t* __restrict__ wsrc, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ expert_ids, int num_experts, int N, int K,
     const uint8_t* __restrict__ x, const int32_t* __restrict__ row_offsets, int M,
     float* __restrict__ y) {
+  static_assert(!kTiled || S == 2, "a tiled unit is two 128-k steps");
   __shared__ ScaleEntry tab[kFp4 ? 256 : 1];
   if constexpr (kFp4) {
     fill_scale_table(tab);
@@ -166,7 +249,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
   const int nbase = (blockIdx.x * kMoeWaves + w) * 16 * NT;
   if (nbase >= N) return;
 
-  // This lane's weight rows (one per tile) and their byte sources.
+  // This lane's weight sources (one per tile).
   const uint8_t* wrow[NT];
   const uint8_t* srow[NT];
   bool tile_ok[NT];
@@ -178,16 +261,20 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
       return;
     }
   }
+  const int64_t ebytes = (int64_t)N * K / (kFp4 ? 2 : 1);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int n = nbase + 16 * j + r16;
     tile_ok[j] = nbase + 16 * j < N;
-    const int64_t rowid = ex * N + (tile_ok[j] ? n : 0);
-    if constexpr (kFp4) {
-      wrow[j] = wsrc + rowid * (K / 2) + 16 * S * g;
-      srow[j] = scales + rowid * (K / 32) + S * g;
+    const int n = (tile_ok[j] ? nbase + 16 * j : nbase) + r16;
+    if constexpr (kTiled) {
+      const int64_t unit0 = (int64_t)(n / 16) * (K / kUnitK);
+      wrow[j] = wsrc + ex * ebytes + unit0 * (kFp4 ? 2048 : 4096) + lane * 16;
+      srow[j] = kFp4 ? scales + ex * ((int64_t)N * K / 32) + unit0 * 128 + lane * 2 : nullptr;
+    } else if constexpr (kFp4) {
+      wrow[j] = wsrc + (ex * N + n) * (K / 2) + 16 * S * g;
+      srow[j] = scales + (ex * N + n) * (K / 32) + S * g;
     } else {
-      wrow[j] = wsrc + rowid * K + 32 * S * g;
+      wrow[j] = wsrc + (ex * N + n) * K + 32 * S * g;
       srow[j] = nullptr;
     }
   }
@@ -198,52 +285,35 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
     const int pbase = pass * 16 * RT;
     f32x4 acc[RT][NT];
     const uint8_t* xrow[RT];
-    bool xok[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int r = pbase + 16 * t + r16;
-      xok[t] = r < count;
-      xrow[t] = x + (int64_t)(row0 + (xok[t] ? r : 0)) * K + 32 * S * g;
+      xrow[t] = x + (int64_t)(row0 + (r < count ? r : 0)) * K + 32 * S * g;
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[t][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    u32x4 raw[NT][kRaw];
-    uint32_t sc[NT];
-    load_weights<NT, kRaw, S, kFp4>(raw, sc, wrow, srow, tile_ok, 0);
-    for (int st = 0; st < steps; ++st) {
-      u32x4 cur[NT][kRaw];
-      uint32_t csc[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        csc[j] = sc[j];
-#pragma unroll
-        for (int q = 0; q < kRaw; ++q) cur[j][q] = raw[j][q];
-      }
-      if (st + 1 < steps) load_weights<NT, kRaw, S, kFp4>(raw, sc, wrow, srow, tile_ok, st + 1);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        i32x8 a[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          if (xok[t]) {
-            const u32x4* xp = (const u32x4*)(xrow[t] + (int64_t)st * 128 * S + 32 * s);
-            a[t] = join(xp[0], xp[1]);
-          } else {
-            a[t] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          i32x8 b;
-          if constexpr (kFp4) {
-            b = convert_block(cur[j][s], tab[(csc[j] >> (8 * s)) & 255]);
-          } else {
-            b = join(cur[j][2 * s], cur[j][2 * s + 1]);
-          }
-#pragma unroll
-          for (int t = 0; t < RT; ++t) acc[t][j] = mfma_fp8(a[t], b, acc[t][j]);
-        }
-      }
+    // Two weight buffers used in turn (a register copy of a buffer in
+    // flight would wait for its loads).
+    u32x4 wa[NT][kRaw], wb[NT][kRaw], xa[RT][2 * S];
+    uint32_t sa[NT], sb[NT];
+    load_weights<NT, kRaw, S, kFp4, kTiled>(wa, sa, wrow, srow, 0);
+    int st = 0;
+    for (; st + 2 < steps; st += 2) {
+      load_tokens<RT, S>(xa, xrow, st);
+      load_weights<NT, kRaw, S, kFp4, kTiled>(wb, sb, wrow, srow, st + 1);
+      super_step<NT, RT, S, kFp4, kRaw>(acc, wa, sa, xa, tab);
+      load_tokens<RT, S>(xa, xrow, st + 1);
+      load_weights<NT, kRaw, S, kFp4, kTiled>(wa, sa, wrow, srow, st + 2);
+      super_step<NT, RT, S, kFp4, kRaw>(acc, wb, sb, xa, tab);
+    }
+    load_tokens<RT, S>(xa, xrow, st);
+    if (st + 1 < steps) {
+      load_weights<NT, kRaw, S, kFp4, kTiled>(wb, sb, wrow, srow, st + 1);
+      super_step<NT, RT, S, kFp4, kRaw>(acc, wa, sa, xa, tab);
+      load_tokens<RT, S>(xa, xrow, st + 1);
+      super_step<NT, RT, S, kFp4, kRaw>(acc, wb, sb, xa, tab);
+    } else {
+      super_step<NT, RT, S, kFp4, kRaw>(acc, wa, sa, xa, tab);
     }
     // Result lane l holds weight row (l & 15) of each tile and token rows
     // 4 g .. 4 g + 3 of each 16-row tile.
@@ -262,72 +332,108 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
   }
 }
 
-// Conversion to a workspace: thread-block rows of 128 elements (four MX
-// blocks: 64 code bytes, four scale bytes) -> 128 E4M3 bytes.
+// Conversion: one thread per MX block (32 elements: 16 code bytes, one
+// scale) -> 32 E4M3 bytes.  The input is in either layout; the output is
+// row-major ([n_act, N, K], blocks in row order) or in unit order (the
+// staged pipeline's workspace: a block's 32 bytes are pieces 2 q and 2 q + 1
+// of its lane in a 4 KB unit).  Threads walk the output in storage order.
+template <bool kTiledOut>
 __global__ __launch_bounds__(kMoeThreads) void mxfp4_to_fp8_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int tiled_in,
     const int32_t* __restrict__ expert_ids, int num_experts, int N, int K, int n_act,
     uint8_t* __restrict__ w8) {
   __shared__ ScaleEntry tab[256];
   fill_scale_table(tab);
   __syncthreads();
-  const int per_row = K / 128;
-  const int64_t per_expert = (int64_t)N * per_row;
+  const int kbs = K / 32;
+  const int64_t per_expert = (int64_t)N * kbs;
   const int64_t total = per_expert * n_act;
   for (int64_t u = (int64_t)blockIdx.x * kMoeThreads + threadIdx.x; u < total;
        u += (int64_t)gridDim.x * kMoeThreads) {
     const int i = (int)(u / per_expert);
     const int64_t rem = u - (int64_t)i * per_expert;
-    const int64_t n = rem / per_row;
-    const int q = (int)(rem - n * per_row);
-    int64_t ex = expert_ids[i];
+    int64_t n, kb, out;
+    if constexpr (kTiledOut) {
+      // rem = ((tile * units + unit) * 2 + q) * 64 + lane
+      const int lane = (int)(rem % 64), q = (int)((rem / 64) % 2);
+      const int64_t unit = rem / 128;  // tile * (K / 256) + unit within the tile
+      n = (unit / (K / kUnitK)) * 16 + lane % 16;
+      kb = (unit % (K / kUnitK)) * 8 + (lane / 16) * 2 + q;
+      out = (int64_t)i * N * K + unit * 4096 + 2 * q * 1024 + lane * 16;
+    } else {
+      n = rem / kbs;
+      kb = rem % kbs;
+      out = ((int64_t)i * N + n) * K + 32 * kb;
+    }
+    const int64_t ex = expert_ids[i];
     if (kCheckBounds && (ex < 0 || ex >= num_experts)) {
       raise_error(kErrIndex);
       continue;
     }
-    const int64_t rowid = ex * N + n;
-    const u32x4* src = (const u32x4*)(codes + rowid * (K / 2) + 64 * q);
-    const uint32_t sc = *(const uint32_t*)(scales + rowid * (K / 32) + 4 * q);
-    u32x4* dst = (u32x4*)(w8 + ((int64_t)i * N + n) * K + 128 * q);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const u32x4 raw = __builtin_nontemporal_load(src + b);
-      const ScaleEntry& t = tab[(sc >> (8 * b)) & 255];
-      const i32x8 o = convert_block(raw, t);
-      dst[2 * b] = (u32x4){(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
-      dst[2 * b + 1] = (u32x4){(uint32_t)o[4], (uint32_t)o[5], (uint32_t)o[6], (uint32_t)o[7]};
-    }
+    const u32x4 raw = __builtin_nontemporal_load(
+        (const u32x4*)(codes + ex * (int64_t)N * (K / 2) + code_offset(tiled_in, n, kb, N, K)));
+    const ScaleEntry& t =
+        tab[scales[ex * (int64_t)N * (K / 32) + scale_offset(tiled_in, n, kb, N, K)]];
+    const i32x8 o = convert_block(raw, t);
+    const u32x4 lo = {(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
+    const u32x4 hi = {(uint32_t)o[4], (uint32_t)o[5], (uint32_t)o[6], (uint32_t)o[7]};
+    *(u32x4*)(w8 + out) = lo;
+    *(u32x4*)(w8 + out + (kTiledOut ? 1024 : 16)) = hi;
   }
 }
 
-template <bool kFp4, int NT, int RT, int S>
+// Row-major MXFP4 -> unit order (a byte permutation): one thread per MX
+// block, walking the output in storage order.
+__global__ __launch_bounds__(kMoeThreads) void mxfp4_pack_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int E, int N, int K,
+    uint8_t* __restrict__ codes_out, uint8_t* __restrict__ scales_out) {
+  const int64_t per_expert = (int64_t)N * (K / 32);
+  const int64_t total = per_expert * E;
+  for (int64_t u = (int64_t)blockIdx.x * kMoeThreads + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * kMoeThreads) {
+    const int64_t e = u / per_expert, rem = u - e * per_expert;
+    const int lane = (int)(rem % 64), q = (int)((rem / 64) % 2);
+    const int64_t unit = rem / 128;
+    const int64_t n = (unit / (K / kUnitK)) * 16 + lane % 16;
+    const int64_t kb = (unit % (K / kUnitK)) * 8 + (lane / 16) * 2 + q;
+    const int64_t cbase = e * N * (K / 2), sbase = e * N * (K / 32);
+    *(u32x4*)(codes_out + cbase + code_offset(true, n, kb, N, K)) =
+        *(const u32x4*)(codes + cbase + code_offset(false, n, kb, N, K));
+    scales_out[sbase + scale_offset(true, n, kb, N, K)] =
+        scales[sbase + scale_offset(false, n, kb, N, K)];
+  }
+}
+
+template <bool kFp4, bool kTiled, int NT, int RT, int S>
 void launch_moe(const uint8_t* wsrc, const uint8_t* scales, const int32_t* expert_ids,
                 int num_experts, int N, int K, const uint8_t* x, const int32_t* row_offsets,
                 int n_act, int M, int max_rows, float* y, hipStream_t stream) {
   const int nblocks = (N + 16 * NT * kMoeWaves - 1) / (16 * NT * kMoeWaves);
   const int passes = max_rows < 1 ? 1 : (max_rows + 16 * RT - 1) / (16 * RT);
   const dim3 grid((unsigned)nblocks, (unsigned)n_act, (unsigned)(passes > 65535 ? 65535 : passes));
-  hipLaunchKernelGGL((moe_gemm_kernel<NT, RT, S, kFp4>), grid, dim3(kMoeThreads), 0, stream,
-                     wsrc, scales, expert_ids, num_experts, N, K, x, row_offsets, M, y);
+  hipLaunchKernelGGL((moe_gemm_kernel<NT, RT, S, kFp4, kTiled>), grid, dim3(kMoeThreads), 0,
+                     stream, wsrc, scales, expert_ids, num_experts, N, K, x, row_offsets, M, y);
 }
 
-// Row-tile count and super-step by size: one 16-row tile for decode-sized
-// batches (the weights are read once whatever the row count), up to four
-// tiles (64 rows) a pass for larger ones.
-template <bool kFp4>
+// Row tiles a pass by size: one 16-row tile for decode-sized batches (the
+// weights are read once whatever the row count), up to four (64 rows) for
+// larger ones.  Super-steps of 256 k (the tiled unit; row-major weights
+// with K % 256 != 0 take 128).
+template <bool kFp4, bool kTiled>
 void dispatch_moe(const uint8_t* wsrc, const uint8_t* scales, const int32_t* expert_ids,
                   int num_experts, int N, int K, const uint8_t* x, const int32_t* row_offsets,
                   int n_act, int M, int max_rows, float* y, hipStream_t stream) {
-#define DSA_MOE_LAUNCH(NT, RT, S)                                                              \
-  launch_moe<kFp4, NT, RT, S>(wsrc, scales, expert_ids, num_experts, N, K, x, row_offsets, \
-                              n_act, M, max_rows, y, stream)
-  const bool s4 = K % 512 == 0;
-  if (max_rows <= 16) {
-    if (s4) DSA_MOE_LAUNCH(2, 1, 4); else DSA_MOE_LAUNCH(2, 1, 1);
-  } else if (max_rows <= 32) {
-    if (s4) DSA_MOE_LAUNCH(2, 2, 4); else DSA_MOE_LAUNCH(2, 2, 1);
-  } else {
-    if (s4) DSA_MOE_LAUNCH(2, 4, 4); else DSA_MOE_LAUNCH(2, 4, 1);
+#define DSA_MOE_LAUNCH(RT, S)                                                              \
+  launch_moe<kFp4, kTiled, 2, RT, S>(wsrc, scales, expert_ids, num_experts, N, K, x,      \
+                                     row_offsets, n_act, M, max_rows, y, stream)
+  if (kTiled || K % kUnitK == 0) {
+    if (max_rows <= 16) DSA_MOE_LAUNCH(1, 2);
+    else if (max_rows <= 32) DSA_MOE_LAUNCH(2, 2);
+    else DSA_MOE_LAUNCH(4, 2);
+  } else if constexpr (!kTiled) {
+    if (max_rows <= 16) DSA_MOE_LAUNCH(1, 1);
+    else if (max_rows <= 32) DSA_MOE_LAUNCH(2, 1);
+    else DSA_MOE_LAUNCH(4, 1);
   }
 #undef DSA_MOE_LAUNCH
 }
@@ -341,21 +447,33 @@ dsa_status_t check_moe_common(int N, int K, const uint8_t* x, const int32_t* row
   return DSA_OK;
 }
 
-dsa_status_t check_weights(const dsa_mxfp4_weights_t* w, const int32_t* expert_ids) {
-  if (!w || !w->codes || !w->scales || !expert_ids) return DSA_ERR_NULL;
+dsa_status_t check_weights(const dsa_mxfp4_weights_t* w) {
+  if (!w || !w->codes || !w->scales) return DSA_ERR_NULL;
   if (w->num_experts < 1 || w->N < 1 || w->K < 1) return DSA_ERR_SHAPE;
-  if (w->K % 128 || w->N % 16) return DSA_ERR_UNSUPPORTED;
+  if (w->layout != DSA_MXFP4_ROW_MAJOR && w->layout != DSA_MXFP4_TILED) return DSA_ERR_SHAPE;
+  if (w->K % 128 || w->N % 16 || (w->layout == DSA_MXFP4_TILED && w->K % kUnitK))
+    return DSA_ERR_UNSUPPORTED;
   if (!aligned16(w->codes) || ((uintptr_t)w->scales & 3)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
+unsigned grid_for(int64_t threads) {
+  const int64_t blocks = (threads + kMoeThreads - 1) / kMoeThreads;
+  return (unsigned)(blocks < 16384 ? blocks : 16384);
+}
+
 dsa_status_t convert_launch(const dsa_mxfp4_weights_t* w, const int32_t* expert_ids, int n_act,
-                            uint8_t* w8, hipStream_t stream) {
-  const int64_t units = (int64_t)n_act * w->N * (w->K / 128);
-  const int64_t blocks = (units + kMoeThreads - 1) / kMoeThreads;
-  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-  hipLaunchKernelGGL(mxfp4_to_fp8_kernel, dim3(grid), dim3(kMoeThreads), 0, stream, w->codes,
-                     w->scales, expert_ids, w->num_experts, w->N, w->K, n_act, w8);
+                            uint8_t* w8, bool tiled_out, hipStream_t stream) {
+  const unsigned grid = grid_for((int64_t)n_act * w->N * (w->K / 32));
+  const int tiled_in = w->layout == DSA_MXFP4_TILED;
+  if (tiled_out)
+    hipLaunchKernelGGL(mxfp4_to_fp8_kernel<true>, dim3(grid), dim3(kMoeThreads), 0, stream,
+                       w->codes, w->scales, tiled_in, expert_ids, w->num_experts, w->N, w->K,
+                       n_act, w8);
+  else
+    hipLaunchKernelGGL(mxfp4_to_fp8_kernel<false>, dim3(grid), dim3(kMoeThreads), 0, stream,
+                       w->codes, w->scales, tiled_in, expert_ids, w->num_experts, w->N, w->K,
+                       n_act, w8);
   return launch_status();
 }
 
@@ -365,33 +483,54 @@ uint32_t take_bounds_error_moe(hipStream_t stream) { return take_bounds_error(st
 
 }  // namespace dsa
 
+extern "C" dsa_status_t dsa_mxfp4_pack(const dsa_mxfp4_weights_t* w, uint8_t* codes_tiled,
+                                       uint8_t* scales_tiled, hipStream_t stream) {
+  using namespace dsa;
+  dsa_status_t st = check_weights(w);
+  if (st != DSA_OK) return st;
+  if (!codes_tiled || !scales_tiled) return DSA_ERR_NULL;
+  if (w->layout != DSA_MXFP4_ROW_MAJOR) return DSA_ERR_SHAPE;
+  if (w->K % kUnitK || !aligned16(codes_tiled)) return DSA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != DSA_OK) return st;
+  const unsigned grid = grid_for((int64_t)w->num_experts * w->N * (w->K / 32));
+  hipLaunchKernelGGL(mxfp4_pack_kernel, dim3(grid), dim3(kMoeThreads), 0, stream, w->codes,
+                     w->scales, w->num_experts, w->N, w->K, codes_tiled, scales_tiled);
+  return launch_status();
+}
+
 extern "C" dsa_status_t dsa_moe_gemm_mxfp4(const dsa_mxfp4_weights_t* w, const uint8_t* x,
                                            const int32_t* expert_ids, const int32_t* row_offsets,
                                            int32_t n_act, int32_t M, int32_t max_rows, float* y,
                                            hipStream_t stream) {
   using namespace dsa;
-  dsa_status_t st = check_weights(w, expert_ids);
+  dsa_status_t st = check_weights(w);
   if (st != DSA_OK) return st;
+  if (!expert_ids) return DSA_ERR_NULL;
   st = check_moe_common(w->N, w->K, x, row_offsets, n_act, M, y);
   if (st != DSA_OK) return st;
   st = check_device();
   if (st != DSA_OK) return st;
-  dispatch_moe<true>(w->codes, w->scales, expert_ids, w->num_experts, w->N, w->K, x, row_offsets,
-                     n_act, M, max_rows, y, stream);
+  if (w->layout == DSA_MXFP4_TILED)
+    dispatch_moe<true, true>(w->codes, w->scales, expert_ids, w->num_experts, w->N, w->K, x,
+                             row_offsets, n_act, M, max_rows, y, stream);
+  else
+    dispatch_moe<true, false>(w->codes, w->scales, expert_ids, w->num_experts, w->N, w->K, x,
+                              row_offsets, n_act, M, max_rows, y, stream);
   return launch_status();
 }
 
 extern "C" dsa_status_t dsa_mxfp4_to_fp8(const dsa_mxfp4_weights_t* w, const int32_t* expert_ids,
                                          int32_t n_act, uint8_t* w8, hipStream_t stream) {
   using namespace dsa;
-  dsa_status_t st = check_weights(w, expert_ids);
+  dsa_status_t st = check_weights(w);
   if (st != DSA_OK) return st;
-  if (!w8) return DSA_ERR_NULL;
+  if (!w8 || !expert_ids) return DSA_ERR_NULL;
   if (n_act < 1 || n_act > 65535) return DSA_ERR_SHAPE;
   if (!aligned16(w8)) return DSA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != DSA_OK) return st;
-  return convert_launch(w, expert_ids, n_act, w8, stream);
+  return convert_launch(w, expert_ids, n_act, w8, false, stream);
 }
 
 extern "C" dsa_status_t dsa_moe_gemm_fp8(const uint8_t* w8, int32_t N, int32_t K, const uint8_t* x,
@@ -404,8 +543,8 @@ extern "C" dsa_status_t dsa_moe_gemm_fp8(const uint8_t* w8, int32_t N, int32_t K
   if (!aligned16(w8)) return DSA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != DSA_OK) return st;
-  dispatch_moe<false>(w8, nullptr, nullptr, n_act, N, K, x, row_offsets, n_act, M, max_rows, y,
-                      stream);
+  dispatch_moe<false, false>(w8, nullptr, nullptr, n_act, N, K, x, row_offsets, n_act, M,
+                             max_rows, y, stream);
   return launch_status();
 }
 
@@ -421,11 +560,13 @@ extern "C" dsa_status_t dsa_moe_gemm_staged(const dsa_mxfp4_weights_t* w, const 
                                             hipStream_t stream, hipStream_t conv_stream,
                                             hipEvent_t* events) {
   using namespace dsa;
-  dsa_status_t st = check_weights(w, expert_ids);
+  dsa_status_t st = check_weights(w);
   if (st != DSA_OK) return st;
+  if (!expert_ids) return DSA_ERR_NULL;
   st = check_moe_common(w->N, w->K, x, row_offsets, n_act, M, y);
   if (st != DSA_OK) return st;
-  if (!workspace || !events || !events[0] || !events[1] || !events[2] || !events[3])
+  if (!workspace || !events || !events[0] || !events[1] || !events[2] || !events[3] ||
+      !events[4])
     return DSA_ERR_NULL;
   if (conv_stream == stream) return DSA_ERR_SHAPE;
   if (!aligned16(workspace)) return DSA_ERR_UNSUPPORTED;
@@ -435,19 +576,29 @@ extern "C" dsa_status_t dsa_moe_gemm_staged(const dsa_mxfp4_weights_t* w, const 
   const int chunk = (int)(chunk64 < n_act ? chunk64 : n_act);
   st = check_device();
   if (st != DSA_OK) return st;
+  // The workspace holds converted weights in unit order whenever K allows.
+  const bool tiled = w->K % kUnitK == 0;
   uint8_t* half[2] = {(uint8_t*)workspace, (uint8_t*)workspace + (size_t)chunk * expert_bytes};
   hipEvent_t* ready = events;      // half h holds converted weights
   hipEvent_t* free_ = events + 2;  // the last product reading half h has finished
+  // The conversions come after everything enqueued on `stream` so far.
+  if (hipEventRecord(events[4], stream) != hipSuccess ||
+      hipStreamWaitEvent(conv_stream, events[4], 0) != hipSuccess)
+    return DSA_ERR_HIP;
   for (int c0 = 0, c = 0; c0 < n_act; c0 += chunk, ++c) {
     const int h = c & 1, n = n_act - c0 < chunk ? n_act - c0 : chunk;
     if (hipStreamWaitEvent(conv_stream, free_[h], 0) != hipSuccess) return DSA_ERR_HIP;
-    st = convert_launch(w, expert_ids + c0, n, half[h], conv_stream);
+    st = convert_launch(w, expert_ids + c0, n, half[h], tiled, conv_stream);
     if (st != DSA_OK) return st;
     if (hipEventRecord(ready[h], conv_stream) != hipSuccess ||
         hipStreamWaitEvent(stream, ready[h], 0) != hipSuccess)
       return DSA_ERR_HIP;
-    dispatch_moe<false>(half[h], nullptr, nullptr, n, w->N, w->K, x, row_offsets + c0, n, M,
-                        max_rows, y, stream);
+    if (tiled)
+      dispatch_moe<false, true>(half[h], nullptr, nullptr, n, w->N, w->K, x, row_offsets + c0, n,
+                                M, max_rows, y, stream);
+    else
+      dispatch_moe<false, false>(half[h], nullptr, nullptr, n, w->N, w->K, x, row_offsets + c0,
+                                 n, M, max_rows, y, stream);
     st = launch_status();
     if (st != DSA_OK) return st;
     if (hipEventRecord(free_[h], stream) != hipSuccess) return DSA_ERR_HIP;

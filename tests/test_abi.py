@@ -270,7 +270,7 @@ def test_moe_validation(L):
     assert L.dsa_moe_staged_ws(64, 256, 3) == 2 * 3 * 64 * 256
     assert L.dsa_moe_staged_ws(64, 256, 0) == 0
     s = L.dsa_moe_gemm_staged
-    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    ev = (ctypes.c_void_p * 5)(FAKE, FAKE, FAKE, FAKE, FAKE)
     ws = L.dsa_moe_staged_ws(64, 256, 1)
 
     def staged(ws_bytes=ws, stream=None, conv=FAKE, events=ev):
@@ -280,5 +280,6 @@ def test_moe_validation(L):
     assert staged() == 5
     assert staged(ws_bytes=ws - 1) == 4                 # not even one expert a half
     assert staged(events=None) == 1
-    assert staged(events=(ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)) == 1
+    assert staged(events=(ctypes.c_void_p * 5)(FAKE, None, FAKE, FAKE, FAKE)) == 1
+    assert staged(events=(ctypes.c_void_p * 5)(FAKE, FAKE, FAKE, FAKE, None)) == 1
     assert staged(conv=None) == 2                       # conversion stream == product stream

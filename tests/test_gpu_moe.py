@@ -47,7 +47,20 @@ def accumulation_bound(x, w8_list, ids_rows, K):
     return [(K + 1) * 2.0 ** -24 * b for b in bounds]
 
 
-def run_case(wl, paths=("fused", "fp8", "staged"), exact=True, chunk=2):
+def tiled_layout_host(codes, scales):
+    """The tiled byte order as the header defines it, written out with numpy
+    index arithmetic (test-side; no kernel code)."""
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    c = codes.reshape(E, N // 16, 16, K // 256, 4, 2, 16)      # e, t, r, u, g, h, bytes
+    c = c.transpose(0, 1, 3, 5, 4, 2, 6)                       # e, t, u, h, g, r, bytes
+    s_ = scales.reshape(E, N // 16, 16, K // 256, 4, 2)        # e, t, r, u, g, h
+    s_ = s_.transpose(0, 1, 3, 4, 2, 5)                        # e, t, u, g, r, h
+    return (np.ascontiguousarray(c).reshape(E, N, K2),
+            np.ascontiguousarray(s_).reshape(E, N, K // 32))
+
+
+def run_case(wl, paths=("fused", "tiled", "fp8", "staged"), exact=True, chunk=2):
     ids, offs, max_rows = synth.routing(wl)
     codes, scales = synth.host_weights(wl)
     x = synth.host_tokens(wl)
@@ -59,6 +72,8 @@ def run_case(wl, paths=("fused", "fp8", "staged"), exact=True, chunk=2):
     outs = {}
     if "fused" in paths:
         outs["fused"] = dsa.moe_gemm_mxfp4(ex, d_x, d_ids, d_offs, max_rows)
+    if "tiled" in paths and wl.K % 256 == 0:
+        outs["tiled"] = dsa.moe_gemm_mxfp4(ex.tiled(), d_x, d_ids, d_offs, max_rows)
     if "fp8" in paths:
         w8 = dsa.mxfp4_to_fp8(ex, d_ids)
         outs["fp8"] = dsa.moe_gemm_fp8(w8, d_x, d_offs, max_rows)
@@ -102,6 +117,22 @@ def test_conversion_every_scale_and_code():
     d_codes, d_scales, d_ids = to_dev(codes, scales, ids)
     got = dsa.mxfp4_to_fp8(dsa.Experts(d_codes, d_scales), d_ids).cpu().numpy()
     np.testing.assert_array_equal(got, ref)
+
+
+def test_pack_is_the_documented_byte_order():
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 256, (3, 48, 256), dtype=np.uint8)
+    scales = rng.integers(0, 256, (3, 48, 16), dtype=np.uint8)
+    d_codes, d_scales = to_dev(codes, scales)
+    t = dsa.Experts(d_codes, d_scales).tiled()
+    c2, s2 = tiled_layout_host(codes, scales)
+    np.testing.assert_array_equal(t.tensors[0].cpu().numpy(), c2)
+    np.testing.assert_array_equal(t.tensors[1].cpu().numpy(), s2)
+    # the conversion reads either layout to the same row-major result
+    ids = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
+    a = dsa.mxfp4_to_fp8(dsa.Experts(d_codes, d_scales), ids)
+    b = dsa.mxfp4_to_fp8(t, ids)
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("K", [512, 384, 2048])
@@ -204,6 +235,26 @@ def test_staged_pipeline_on_a_side_stream():
     np.testing.assert_array_equal(y.cpu().numpy(), ref)
 
 
+def test_staged_pipeline_orders_after_work_already_on_the_stream():
+    # weights packed on the current stream just before the call, and a
+    # workspace whose memory a just-freed tensor held: the conversions on the
+    # second stream must come after both
+    wl = small("order", 8, 64, 512, 30, 126, 128, "int", 95)
+    ids, offs, max_rows = synth.routing(wl)
+    codes, scales = synth.host_weights(wl)
+    x = synth.host_tokens(wl)
+    ref = oracle.moe_gemm(x, offs, ids, codes, scales, wl.N, wl.K)
+    d = to_dev(codes, scales, x, ids, offs)
+    for rep in range(3):
+        big = torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(rep)
+        del big  # its block returns to the allocator with the fill still pending
+        st = dsa.MoeStaged(wl.N, wl.K, 2)
+        y = st(dsa.Experts(d[0], d[1]).tiled(), d[2], d[3], d[4], max_rows)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref, err_msg=f"rep {rep}")
+        del st
+
+
 def test_debug_build_flags_bad_routing():
     D = dsa.debug_lib()
     wl = small("dbg", 4, 16, 256, 10, 126, 128, "int", 101)
@@ -240,11 +291,14 @@ def test_full_size_layer_sampled_experts(make):
     x = synth.device_tokens(wl)
     d_ids, d_offs = to_dev(ids, offs)
     ex = dsa.Experts(codes, scales)
-    y = dsa.moe_gemm_mxfp4(ex, x, d_ids, d_offs, max_rows)
+    y = dsa.moe_gemm_mxfp4(ex.tiled(), x, d_ids, d_offs, max_rows)
+    y1 = dsa.moe_gemm_mxfp4(ex, x, d_ids, d_offs, max_rows)
     st = dsa.MoeStaged(wl.N, wl.K, 16)
     y2 = st(ex, x, d_ids, d_offs, max_rows)
     torch.cuda.synchronize()
+    assert torch.equal(y, y1), "tiled weights differ from row-major weights"
     assert torch.equal(y, y2), "staged pipeline differs from the fused product"
+    del y1, y2, st
     counts = np.diff(offs)
     for i in sorted({0, int(np.argmax(counts)), len(ids) - 1}):
         e = int(ids[i])

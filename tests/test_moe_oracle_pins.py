@@ -72,7 +72,7 @@ def test_hand_worked_block(oracle_lib):
     assert (w8[0, 0, 4:] == 0).all()  # code 0 -> +0
 
 
-def _random_mxfp4(rng, experts, N, K, scale_lo=122, scale_hi=133):
+def _random_mxfp4(rng, experts, N, K, scale_lo=119, scale_hi=133):
     codes = rng.integers(0, 256, (experts, N, K // 2), dtype=np.uint8)
     scales = rng.integers(scale_lo, scale_hi + 1, (experts, N, K // 32), dtype=np.uint8)
     return codes, scales
@@ -89,7 +89,9 @@ def _decode_mxfp4(codes, scales, K):
 
 
 def test_conversion_is_exact_in_the_exact_scale_range(oracle_lib):
-    # scales 2^-5 .. 2^6 keep every scaled E2M1 value an E4M3 normal number
+    # scales 2^-8 .. 2^6 keep every scaled E2M1 value an E4M3 number: at 2^-8
+    # the smallest, 0.5 * 2^-8, is the smallest E4M3 subnormal 2^-9; at 2^6 the
+    # largest, 6 * 2^6 = 384, is below 448
     rng = np.random.default_rng(1)
     codes, scales = _random_mxfp4(rng, 3, 48, 128)
     w8 = oracle_lib.mxfp4_to_fp8(codes, scales, [2, 0], 48, 128)
@@ -97,6 +99,16 @@ def test_conversion_is_exact_in_the_exact_scale_range(oracle_lib):
     got = torch.from_numpy(w8).view(torch.float8_e4m3fn).double().numpy()
     np.testing.assert_array_equal(got[0], dec[2])
     np.testing.assert_array_equal(got[1], dec[0])
+
+
+def test_exact_range_is_tight(oracle_lib):
+    # one step beyond either end some scaled element is not an E4M3 number
+    half_at_118 = oracle_lib.e4m3_value(oracle_lib.mxfp4_to_fp8(
+        np.full((1, 16, 16), 0x11, np.uint8), np.full((1, 16, 1), 118, np.uint8), [0], 16, 32)[0, 0, 0])
+    assert half_at_118 != 0.5 * 2.0 ** -9       # 2^-10 rounds (to 0)
+    six_at_134 = oracle_lib.e4m3_value(oracle_lib.mxfp4_to_fp8(
+        np.full((1, 16, 16), 0x77, np.uint8), np.full((1, 16, 1), 134, np.uint8), [0], 16, 32)[0, 0, 0])
+    assert six_at_134 == 448.0                  # 768 saturates
 
 
 def test_conversion_rounds_and_saturates_outside_it(oracle_lib):
