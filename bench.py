@@ -323,6 +323,71 @@ def bench_prefill(timer, reps, warmup, log):
     return res, cw
 
 
+FP8_MFMA_PEAK_TF = 5000.0  # MI355X dense FP8 matrix peak (TFLOP/s)
+
+
+def moe_layer_bytes(wl, n_act, M):
+    """Algorithmic HBM bytes of one expert-layer product: the listed
+    experts' MXFP4 weights once (codes + scales, 17/32 byte an element), the
+    token rows once (E4M3) and the fp32 result once."""
+    return n_act * wl.N * wl.K * 17 // 32 + M * wl.K + M * wl.N * 4
+
+
+def bench_moe(timer, steps, warmup, log):
+    """The MoE expert product of one layer (MXFP4 weights converted to FP8
+    just before use) at the decode and prefill batch sizes: the fused call on
+    tiled weights (the headline of each), and beside it the fused call on
+    row-major weights, the conversion alone and the staged two-stream
+    pipeline."""
+    import torch
+
+    import sparse_attention_long_dsa_amd as dsa
+    from dsa_synth import moe as synth
+
+    out = {}
+    for make in (synth.decode_layer, synth.prefill_layer):
+        wl = make()
+        ids, offs, max_rows = synth.routing(wl)
+        n_act, M = len(ids), int(offs[-1])
+        codes, scales = synth.device_weights(wl)
+        x = synth.device_tokens(wl)
+        d_ids = torch.from_numpy(ids).cuda()
+        d_offs = torch.from_numpy(offs).cuda()
+        rowmajor = dsa.Experts(codes, scales)
+        tiled = rowmajor.tiled()
+        y = torch.empty((M, wl.N), dtype=torch.float32, device="cuda")
+        staged = dsa.MoeStaged(wl.N, wl.K, 16)
+        w8 = torch.empty((16, wl.N, wl.K), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        calls = [lambda: dsa.moe_gemm_mxfp4(tiled, x, d_ids, d_offs, max_rows, out=y)]
+        parts = [calls[0],
+                 lambda: dsa.moe_gemm_mxfp4(rowmajor, x, d_ids, d_offs, max_rows, out=y),
+                 lambda: dsa.mxfp4_to_fp8(tiled, d_ids[:16], out=w8),
+                 lambda: staged(tiled, x, d_ids, d_offs, max_rows, out=y)]
+        r = timer.run(calls, steps, warmup, breakdown=parts)
+        ms = r["median_ms"]
+        nbytes = moe_layer_bytes(wl, n_act, M)
+        flops = 2 * M * wl.N * wl.K
+        conv_bytes = 16 * wl.N * wl.K * (17 / 32 + 1)
+        e = {"workload": wl.name, "experts_listed": n_act, "rows": M, "max_rows": max_rows,
+             "N": wl.N, "K": wl.K, "scale_codes": [wl.scale_lo, wl.scale_hi],
+             "ms": round(ms, 4), "ms_min": round(r["min_ms"], 4),
+             "ms_rowmajor_weights": round(r["per_call_ms"][1], 4),
+             "ms_convert_16_experts": round(r["per_call_ms"][2], 4),
+             "convert_gbs": round(conv_bytes / (r["per_call_ms"][2] * 1e-3) / 1e9, 1),
+             "ms_staged_pipeline": round(r["per_call_ms"][3], 4),
+             "algorithmic_bytes": nbytes, "flops": flops,
+             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+             "fp8_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_MFMA_PEAK_TF, 4)}
+        log(f"{wl.name}: {ms:.3f} ms, {e['gbs']} GB/s, {e['tflops']} TFLOP/s")
+        out[make.__name__] = e
+        del codes, scales, x, rowmajor, tiled, y, staged, w8, calls, parts
+        torch.cuda.empty_cache()
+    return out
+
+
 def hbm_probe(log):
     """Achievable HBM read bandwidth: the streaming-read probe over a 2 GiB
     buffer, a few grid sizes, the best median of 5 reads each."""
@@ -459,6 +524,8 @@ def main():
                     help="skip the other full-size decode batches")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="skip the MoE expert layers (MXFP4 -> FP8 product)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -539,6 +606,18 @@ def main():
         p, cw = bench_prefill(timer, args.prefill_reps, 2, log)
         res["prefill"] = p
         res["cache_write"] = cw
+    if not args.no_moe:
+        moe = bench_moe(timer, args.steps, args.warmup, log)
+        dec, pre = moe["decode_layer"], moe["prefill_layer"]
+        res["moe"] = {
+            "decode_layer": dict(dec, roofline={
+                "bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dec["hbm_frac"],
+                **({"achievable": probe["gbs"],
+                    "frac_of_achievable": round(dec["gbs"] / probe["gbs"], 4)} if probe else {})}),
+            "prefill_layer": dict(pre, roofline={
+                "bound": "mfma", "achieved": pre["tflops"], "peak": FP8_MFMA_PEAK_TF,
+                "unit": "TFLOP/s", "frac": pre["fp8_mfma_frac"]})}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, log)
     print(json.dumps(res), flush=True)

@@ -332,6 +332,254 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(
   }
 }
 
+// The product kernel for larger expert batches (prefill: a few hundred
+// rows an expert), bound by the matrix cores.  Workgroup (b, i, z) of eight
+// waves (two per SIMD, so one wave's conversion overlaps the other's
+// products): listed expert i, weight rows 256 b .. +256, and the token rows
+// of pass z (the expert's rows cut into ceil(count / 256) equal passes of
+// whole 16-row tiles, at most 16 tiles).  Wave w takes weight rows
+// 64 (w % 4) .. +64 (four 16-row tiles, converted in its registers from the
+// tiled layout) and token tiles w / 4, w / 4 + 2, ... (every other tile, so
+// both waves on a SIMD get half of a short pass).  Token tiles go through
+// LDS, double buffered, in MFMA operand order: each 1 KB block (tile t,
+// step s, half h) is what one wave reads with one 16-byte load a lane.  One
+// barrier a 256-k super-step.  Weights, scales and token rows are read
+// through buffer resources with per-tile offsets in scalar registers, so no
+// per-tile address occupies vector registers.
+constexpr int kBigThreads = 512;
+constexpr int kBigRows = 256;   // token rows a pass
+constexpr int kBigTiles = kBigRows / 16;
+constexpr int kBigNT = 4;       // 16-row weight tiles a wave
+constexpr int kBigWaveTiles = kBigTiles / 2;  // token tiles a wave
+constexpr int kBigN = 4 * kBigNT * 16;        // weight rows a workgroup
+constexpr int kBigStage = kBigTiles * 16 * 16 / kBigThreads;  // staged pieces a thread
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Token staging of one super-step, half H (0 or 1): thread (tile group tg =
+// tid / 256, row r = (tid / 16) % 16, chunk c = tid % 16) moves row r of
+// tiles tg + 2 v, v = H WT / 2 .. (H + 1) WT / 2 - 1, bytes 16 c .. +15 of
+// the super-step's 256 (16 threads read a row's 256 bytes: coalesced).
+// Chunk c = 4 g + p is part p (step p / 2, half p % 2) of operand lane
+// L = 16 g + r.  Inside each 1 KB LDS block (tile, part p) lane L's 16 bytes
+// sit at slot L ^ ((4 p + g) & 15): the 16 lanes of a store group (one row,
+// all (g, p)) and of a load group (one g, all rows) then fall on 16
+// different bank groups.  The tile offset is uniform (a scalar operand);
+// rows past the expert's count read as zeros (buffer bounds).
+__device__ __forceinline__ int big_slot(int p, int L) { return L ^ ((4 * p + (L >> 4)) & 15); }
+
+template <int WT, int H>
+__device__ __forceinline__ void big_stage_load(u32x4 (&xr)[WT / 2], __amdgpu_buffer_rsrc_t xrsrc,
+                                               int voff, int tb, int K, int st) {
+#pragma unroll
+  for (int v = 0; v < WT / 2; ++v) {
+    const int t = tb + 2 * (H * (WT / 2) + v);
+    xr[v] = buf_load16(xrsrc, voff, 16 * t * K + st * kUnitK);
+  }
+}
+template <int WT, int H>
+__device__ __forceinline__ void big_stage_store(u32x4* xs, const u32x4 (&xr)[WT / 2], int xoff,
+                                                int tb) {
+#pragma unroll
+  for (int v = 0; v < WT / 2; ++v) {
+    const int t = tb + 2 * (H * (WT / 2) + v);
+    xs[t * 256 + xoff] = xr[v];
+  }
+}
+
+// One step's weight pieces of the wave's four tiles (16 bytes a lane each)
+// and a super-step's scale pairs.
+__device__ __forceinline__ void big_load_w(u32x4 (&w)[kBigNT], __amdgpu_buffer_rsrc_t wr,
+                                           int lane, int unit0, int units, int st, int s) {
+#pragma unroll
+  for (int j = 0; j < kBigNT; ++j)
+    w[j] = buf_load16(wr, lane * 16, ((unit0 + j * units) + st) * 2048 + s * 1024);
+}
+__device__ __forceinline__ void big_load_s(uint32_t (&sc)[kBigNT], __amdgpu_buffer_rsrc_t sr,
+                                           int lane, int unit0, int units, int st) {
+#pragma unroll
+  for (int j = 0; j < kBigNT; ++j)
+    sc[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, lane * 2, ((unit0 + j * units) + st) * 128, 0);
+}
+
+// Step s of a super-step: the wave's four weight tiles of step (st, s) are
+// converted and their registers refilled at once with step (st + 1, s) --
+// two steps ahead of use (nothing on the last super-step) -- then the
+// converted tiles times the wave's WT token tiles (LDS reads one tile ahead
+// of the products).
+template <int WT, int s, bool kMore>
+__device__ __forceinline__ void big_products(f32x4 (&acc)[WT][kBigNT], u32x4 (&w)[kBigNT],
+                                             const uint32_t (&sc)[kBigNT],
+                                             __amdgpu_buffer_rsrc_t wr, int unit0, int units,
+                                             int st, const u32x4* xs, int tg, int lane,
+                                             const ScaleEntry* tab) {
+  i32x8 b[kBigNT];
+#pragma unroll
+  for (int j = 0; j < kBigNT; ++j) b[j] = convert_block(w[j], tab[(sc[j] >> (8 * s)) & 255]);
+  if (kMore) big_load_w(w, wr, lane, unit0, units, st + 1, s);
+  // tile tg, step s: parts 2 s and 2 s + 1 at this lane's slots
+  const u32x4* src0 = xs + (tg * 4 + s * 2) * 64 + big_slot(2 * s, lane);
+  const u32x4* src1 = xs + (tg * 4 + s * 2 + 1) * 64 + big_slot(2 * s + 1, lane);
+  i32x8 a = join(src0[0], src1[0]);
+#pragma unroll
+  for (int t = 0; t < WT; ++t) {
+    i32x8 an = a;
+    if (t + 1 < WT) an = join(src0[(t + 1) * 512], src1[(t + 1) * 512]);  // tile tg + 2 (t + 1)
+#pragma unroll
+    for (int j = 0; j < kBigNT; ++j) acc[t][j] = mfma_fp8(a, b[j], acc[t][j]);
+    a = an;
+  }
+}
+
+// One super-step st: the first half of token tiles st + 1 is loaded during
+// step 0's products and the second half (with the scales of st + 1) during
+// step 1's; the staged halves go to the other LDS buffer; a barrier ends
+// it.  kLast: the final super-step (no loads of st + 1).
+template <int WT, bool kLast>
+__device__ __forceinline__ void big_super_step(
+    f32x4 (&acc)[WT][kBigNT], u32x4 (&w0)[kBigNT], u32x4 (&w1)[kBigNT], uint32_t (&sc)[kBigNT],
+    uint32_t (&scn)[kBigNT], u32x4 (&xr)[WT / 2], __amdgpu_buffer_rsrc_t wr,
+    __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t xrsrc, int unit0, int units, int xvoff,
+    int xoff, int tg, int K, int st, int lane, const u32x4* xs_cur, u32x4* xs_next,
+    const ScaleEntry* tab) {
+  if (!kLast) big_stage_load<WT, 0>(xr, xrsrc, xvoff, tg, K, st + 1);
+  big_products<WT, 0, !kLast>(acc, w0, sc, wr, unit0, units, st, xs_cur, tg, lane, tab);
+  if (!kLast) {
+    big_load_s(scn, sr, lane, unit0, units, st + 1);
+    big_stage_store<WT, 0>(xs_next, xr, xoff, tg);
+    big_stage_load<WT, 1>(xr, xrsrc, xvoff, tg, K, st + 1);
+  }
+  big_products<WT, 1, !kLast>(acc, w1, sc, wr, unit0, units, st, xs_cur, tg, lane, tab);
+  if (!kLast) {
+    big_stage_store<WT, 1>(xs_next, xr, xoff, tg);
+    __syncthreads();
+  }
+}
+
+// One pass of up to 2 WT token tiles (rows pbase .. pbase + prow - 1 of the
+// expert), every product on all 2 WT tiles (rows past prow are zeros or the
+// next pass's rows, never stored).
+template <int WT>
+__device__ __forceinline__ void big_pass(u32x4 (*xs)[kBigTiles * 4 * 64],
+                                         __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                         __amdgpu_buffer_rsrc_t xrsrc, int unit0, int units,
+                                         int K, int N, int pbase, int prow, int row0, int tid,
+                                         int nbase, const bool (&tile_ok)[kBigNT],
+                                         const ScaleEntry* tab, float* __restrict__ y) {
+  // the wave index through readfirstlane: wave-uniform values derived from
+  // it stay in scalar registers (buffer offsets need them there)
+  const int lane = tid & (kWave - 1), w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int tg = w >> 2;  // token tiles tg, tg + 2, ... (products and staging)
+  const int srow = (tid >> 4) & 15, chunk = tid & 15;
+  const int xoff = (chunk & 3) * 64 + big_slot(chunk & 3, 16 * (chunk >> 2) + srow);
+  const int xvoff = (pbase + srow) * K + 16 * chunk;
+  const int steps = units;
+  f32x4 acc[WT][kBigNT];
+#pragma unroll
+  for (int t = 0; t < WT; ++t)
+#pragma unroll
+    for (int j = 0; j < kBigNT; ++j) acc[t][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  u32x4 w0[kBigNT], w1[kBigNT], xr[WT / 2];
+  uint32_t sa[kBigNT], sb[kBigNT];
+  big_load_w(w0, wr, lane, unit0, units, 0, 0);
+  big_load_w(w1, wr, lane, unit0, units, 0, 1);
+  big_stage_load<WT, 0>(xr, xrsrc, xvoff, tg, K, 0);
+  big_stage_store<WT, 0>(xs[0], xr, xoff, tg);
+  big_stage_load<WT, 1>(xr, xrsrc, xvoff, tg, K, 0);
+  big_load_s(sa, sr, lane, unit0, units, 0);
+  big_stage_store<WT, 1>(xs[0], xr, xoff, tg);
+  __syncthreads();  // the scale table and the first token tiles
+  int st = 0;
+  for (; st + 2 < steps; st += 2) {
+    big_super_step<WT, false>(acc, w0, w1, sa, sb, xr, wr, sr, xrsrc, unit0, units, xvoff, xoff, tg, K,
+                              st, lane, xs[0], xs[1], tab);
+    big_super_step<WT, false>(acc, w0, w1, sb, sa, xr, wr, sr, xrsrc, unit0, units, xvoff, xoff, tg, K,
+                              st + 1, lane, xs[1], xs[0], tab);
+  }
+  if (st + 1 < steps) {
+    big_super_step<WT, false>(acc, w0, w1, sa, sb, xr, wr, sr, xrsrc, unit0, units, xvoff, xoff, tg, K,
+                              st, lane, xs[0], xs[1], tab);
+    big_super_step<WT, true>(acc, w0, w1, sb, sa, xr, wr, sr, xrsrc, unit0, units, xvoff, xoff, tg, K,
+                             st + 1, lane, xs[1], xs[0], tab);
+  } else {
+    big_super_step<WT, true>(acc, w0, w1, sa, sb, xr, wr, sr, xrsrc, unit0, units, xvoff, xoff, tg, K,
+                             st, lane, xs[0], xs[1], tab);
+  }
+#pragma unroll
+  for (int t = 0; t < WT; ++t) {
+    const int tile = tg + 2 * t;
+#pragma unroll
+    for (int j = 0; j < kBigNT; ++j) {
+      if (!tile_ok[j]) continue;
+      const int n = nbase + 16 * j + r16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tile + 4 * g + q;
+        if (r < prow) y[(int64_t)(row0 + pbase + r) * N + n] = acc[t][j][q];
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the LDS tiles before the next pass
+}
+
+__global__ __launch_bounds__(kBigThreads) void moe_gemm_big_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const int32_t* __restrict__ expert_ids, int num_experts, int N, int K,
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ row_offsets, int M,
+    float* __restrict__ y) {
+  __shared__ ScaleEntry tab[256];
+  __shared__ u32x4 xs[2][kBigTiles * 4 * 64];  // [buffer][tile][s][h][lane]
+  fill_scale_table(tab);
+  const int i = blockIdx.y;
+  int row0, count;
+  expert_rows(row_offsets, i, M, row0, count);
+  const int passes = (count + kBigRows - 1) / kBigRows;
+  // Equal passes of whole 16-row tiles.
+  const int per_pass = passes ? ((count + passes - 1) / passes + 15) / 16 * 16 : 0;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int nbase = blockIdx.x * kBigN + (w & 3) * kBigNT * 16;
+  int64_t ex = expert_ids[i];
+  if (kCheckBounds && (ex < 0 || ex >= num_experts)) {
+    if (tid == 0) raise_error(kErrIndex);
+    ex = -1;
+  }
+  if (ex < 0) return;  // uniform over the workgroup, before any barrier
+
+  // Weight tiles past N repeat the expert's first tile (their products are
+  // never stored).
+  const int units = K / kUnitK;
+  const int ntile = nbase < N ? nbase / 16 : 0;
+  bool tile_ok[kBigNT];
+#pragma unroll
+  for (int j = 0; j < kBigNT; ++j) tile_ok[j] = nbase + 16 * j < N;
+  const int unit0 = ntile * units;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + ex * ((int64_t)N * K / 2)), (short)0, N * (K / 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + ex * ((int64_t)N * K / 32)), (short)0, N * (K / 32), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)row0 * K), (short)0, count * K, kRsrcWord3);
+
+  for (int pz = blockIdx.z; pz < passes; pz += gridDim.z) {
+    const int pbase = pz * per_pass;
+    const int prow = min(per_pass, count - pbase);
+    const int pairs = (prow + 31) / 32;  // tile pairs: each wave takes one tile of a pair
+    if (pairs > 6)
+      big_pass<8>(xs, wr, sr, xrsrc, unit0, units, K, N, pbase, prow, row0, tid, nbase, tile_ok, tab, y);
+    else if (pairs > 4)
+      big_pass<6>(xs, wr, sr, xrsrc, unit0, units, K, N, pbase, prow, row0, tid, nbase, tile_ok, tab, y);
+    else if (pairs > 2)
+      big_pass<4>(xs, wr, sr, xrsrc, unit0, units, K, N, pbase, prow, row0, tid, nbase, tile_ok, tab, y);
+    else
+      big_pass<2>(xs, wr, sr, xrsrc, unit0, units, K, N, pbase, prow, row0, tid, nbase, tile_ok, tab, y);
+  }
+}
+
 // Conversion: one thread per MX block (32 elements: 16 code bytes, one
 // scale) -> 32 E4M3 bytes.  The input is in either layout; the output is
 // row-major ([n_act, N, K], blocks in row order) or in unit order (the
@@ -415,9 +663,20 @@ void launch_moe(const uint8_t* wsrc, const uint8_t* scales, const int32_t* exper
                      stream, wsrc, scales, expert_ids, num_experts, N, K, x, row_offsets, M, y);
 }
 
+void launch_moe_big(const uint8_t* wsrc, const uint8_t* scales, const int32_t* expert_ids,
+                    int num_experts, int N, int K, const uint8_t* x, const int32_t* row_offsets,
+                    int n_act, int M, int max_rows, float* y, hipStream_t stream) {
+  const int nblocks = (N + kBigN - 1) / kBigN;
+  const int passes = (max_rows + kBigRows - 1) / kBigRows;
+  const dim3 grid((unsigned)nblocks, (unsigned)n_act, (unsigned)(passes > 65535 ? 65535 : passes));
+  hipLaunchKernelGGL(moe_gemm_big_kernel, grid, dim3(kBigThreads), 0, stream, wsrc, scales,
+                     expert_ids, num_experts, N, K, x, row_offsets, M, y);
+}
+
 // Row tiles a pass by size: one 16-row tile for decode-sized batches (the
-// weights are read once whatever the row count), up to four (64 rows) for
-// larger ones.  Super-steps of 256 k (the tiled unit; row-major weights
+// weights are read once whatever the row count), two up to 32 rows; larger
+// batches on tiled MXFP4 weights take the LDS-staged kernel (256 rows a
+// pass), others four tiles (64 rows) a pass.  Super-steps of 256 k (the tiled unit; row-major weights
 // with K % 256 != 0 take 128).
 template <bool kFp4, bool kTiled>
 void dispatch_moe(const uint8_t* wsrc, const uint8_t* scales, const int32_t* expert_ids,
@@ -429,6 +688,10 @@ void dispatch_moe(const uint8_t* wsrc, const uint8_t* scales, const int32_t* exp
   if (kTiled || K % kUnitK == 0) {
     if (max_rows <= 16) DSA_MOE_LAUNCH(1, 2);
     else if (max_rows <= 32) DSA_MOE_LAUNCH(2, 2);
+    else if (kFp4 && kTiled && (int64_t)M * K <= INT32_MAX &&
+             (int64_t)N * K / 2 <= INT32_MAX)
+      launch_moe_big(wsrc, scales, expert_ids, num_experts, N, K, x, row_offsets, n_act, M,
+                     max_rows, y, stream);
     else DSA_MOE_LAUNCH(4, 2);
   } else if constexpr (!kTiled) {
     if (max_rows <= 16) DSA_MOE_LAUNCH(1, 1);
