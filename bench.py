@@ -56,7 +56,12 @@ KERNEL_SOURCES = {
     "sparse_attn_latent": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
     "attn_combine": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
     "topk": ["topk.hip", "common.h"],
+    "moe_decode": ["moe.hip", "common.h"],
+    "moe_prefill": ["moe.hip", "common.h"],
 }
+# the kernel-name fragment of each key in a counter CSV (default: the key)
+KERNEL_NAME_PART = {"moe_decode": "moe_gemm_kernel<2, 1, 2, true, true>",
+                    "moe_prefill": "moe_gemm_big_kernel"}
 
 
 def traffic_file(kernel):
@@ -380,7 +385,9 @@ def bench_moe(timer, steps, warmup, log):
              "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
              "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-             "fp8_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_MFMA_PEAK_TF, 4)}
+             "fp8_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / FP8_MFMA_PEAK_TF, 4),
+             "traffic": traffic_for("moe_decode" if make is synth.decode_layer
+                                    else "moe_prefill", wl.name)}
         log(f"{wl.name}: {ms:.3f} ms, {e['gbs']} GB/s, {e['tflops']} TFLOP/s")
         out[make.__name__] = e
         del codes, scales, x, rowmajor, tiled, y, staged, w8, calls, parts
@@ -397,7 +404,9 @@ def hbm_probe(log):
     buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     best = None
-    for grid, nt in ((1024, 1), (2048, 1), (4096, 1), (8192, 1), (4096, 0)):
+    modes = {0: "ordinary loads", 1: "non-temporal loads", 2: "per-workgroup regions"}
+    for grid, nt in ((1024, 1), (2048, 1), (4096, 1), (8192, 1), (4096, 0), (4096, 2),
+                     (8192, 2), (16384, 2)):
         sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
         times = []
         for rep in range(6):
@@ -412,15 +421,15 @@ def hbm_probe(log):
             if rep > 0:
                 times.append(a.elapsed_time(b))
         gbs = PROBE_BYTES / (statistics.median(times) * 1e-3) / 1e9
-        log(f"hbm probe: grid {grid} x 256, {'non-temporal' if nt else 'ordinary'} loads: "
-            f"{gbs:.0f} GB/s")
+        log(f"hbm probe: grid {grid} x 256, {modes[nt]}: {gbs:.0f} GB/s")
         if best is None or gbs > best[0]:
             best = (gbs, grid, nt)
     del buf
     torch.cuda.empty_cache()
-    return {"kernel": "hbm_read_kernel (streaming read, 16 B a lane, 8 loads in flight)",
+    return {"kernel": "hbm_read_kernel / hbm_read_chunk_kernel (streaming read, 16 B a lane, "
+                      "8 loads in flight; best of grid sizes and patterns)",
             "bytes": PROBE_BYTES, "gbs": round(best[0], 1), "grid_blocks": best[1],
-            "nontemporal": bool(best[2]), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
+            "pattern": modes[best[2]], "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, budget_s, log):
@@ -493,8 +502,9 @@ def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_w
     """Fold two counter runs of a kernel and two of the plain copy into
     profiles/traffic_KERNEL.json (HBM bytes per launch).  `cname` names the
     copy kernel (the runtime's device-to-device copy)."""
-    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
-    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    part = KERNEL_NAME_PART.get(kernel, kernel)
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", part)
+    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE", part)
     cf = _pmc_per_dispatch(copy_fetch_csv, "FETCH_SIZE", cname)
     cw = _pmc_per_dispatch(copy_write_csv, "WRITE_SIZE", cname)
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
@@ -612,12 +622,12 @@ def main():
         res["moe"] = {
             "decode_layer": dict(dec, roofline={
                 "bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dec["hbm_frac"],
+                "frac": dec["hbm_frac"], "traffic": dec["traffic"],
                 **({"achievable": probe["gbs"],
                     "frac_of_achievable": round(dec["gbs"] / probe["gbs"], 4)} if probe else {})}),
             "prefill_layer": dict(pre, roofline={
                 "bound": "mfma", "achieved": pre["tflops"], "peak": FP8_MFMA_PEAK_TF,
-                "unit": "TFLOP/s", "frac": pre["fp8_mfma_frac"]})}
+                "unit": "TFLOP/s", "frac": pre["fp8_mfma_frac"], "traffic": pre["traffic"]})}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, log)
     print(json.dumps(res), flush=True)

@@ -41,16 +41,42 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restr
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// Chunked variant: workgroup b streams its own contiguous region (vectors
+// b * per_block .. (b + 1) * per_block - 1, per_block a multiple of
+// kThreads * kInFlight), each wave load one contiguous KB, kInFlight loads
+// in flight per lane -- the pattern of a kernel whose workgroups each
+// stream their own weight block.
+__global__ __launch_bounds__(kThreads) void hbm_read_chunk_kernel(const u32x4* __restrict__ src,
+                                                                  int64_t per_block,
+                                                                  uint32_t* __restrict__ sink) {
+  const u32x4* p = src + (int64_t)blockIdx.x * per_block + threadIdx.x;
+  uint32_t acc = 0;
+  for (int64_t i = 0; i < per_block; i += kThreads * kInFlight) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from device buffer `src` once; `sink`
 // receives one word per thread of the grid (grid_blocks * 256 words).
-// nontemporal != 0: non-temporal loads.  Returns 0, or 1 for bad arguments,
-// 2 when the launch fails.
+// nontemporal != 0: non-temporal loads; nontemporal == 2: the chunked
+// pattern, each workgroup reading bytes / grid_blocks contiguous bytes
+// (bytes must be a multiple of grid_blocks * 32768).  Returns 0, or 1 for
+// bad arguments, 2 when the launch fails.
 extern "C" int hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int grid_blocks,
                               int nontemporal, hipStream_t stream) {
   if (!src || !sink || bytes < 16 || bytes % 16 != 0 || grid_blocks < 1) return 1;
-  if (nontemporal)
+  if (nontemporal == 2) {
+    if (bytes % ((int64_t)grid_blocks * kThreads * kInFlight * 16) != 0) return 1;
+    hipLaunchKernelGGL(hbm_read_chunk_kernel, dim3(grid_blocks), dim3(kThreads), 0, stream,
+                       (const u32x4*)src, bytes / 16 / grid_blocks, sink);
+  } else if (nontemporal)
     hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(grid_blocks), dim3(kThreads), 0, stream,
                        (const u32x4*)src, bytes / 16, sink);
   else
