@@ -7,6 +7,7 @@ libdsa.so is missing or cannot load, importing the functions below raises.
 
 The C ABI is declared in include/dsa.h; the names here match it:
   index_score        -> dsa_index_score
+  index_topk_prefill -> dsa_index_topk_prefill
   topk               -> dsa_topk
   sparse_attn_decode -> dsa_sparse_attn_decode
   sparse_attn_prefill-> dsa_sparse_attn_prefill
@@ -134,6 +135,9 @@ def _configure(L):
     L.dsa_index_topk_decode_ws.restype = sz
     L.dsa_index_topk_decode.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, vp, i64, vp, i32, vp,
                                         sz, vp]
+    L.dsa_index_topk_prefill_ws.argtypes = [i32]
+    L.dsa_index_topk_prefill_ws.restype = sz
+    L.dsa_index_topk_prefill.argtypes = [pc, vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
     L.dsa_topk_workspace_size.restype = sz
     L.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, sz, vp]
@@ -154,7 +158,8 @@ def _configure(L):
     L.dsa_moe_gemm_staged.argtypes = [pw, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp]
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
-    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_index_topk_decode, L.dsa_sparse_attn_decode,
+    for f in (L.dsa_index_score, L.dsa_topk, L.dsa_index_topk_decode, L.dsa_index_topk_prefill,
+              L.dsa_sparse_attn_decode,
               L.dsa_sparse_attn_decode_static, L.dsa_sparse_attn_prefill, L.dsa_cache_write,
               L.dsa_check_device_errors, L.dsa_mxfp4_pack, L.dsa_moe_gemm_mxfp4, L.dsa_mxfp4_to_fp8,
               L.dsa_moe_gemm_fp8, L.dsa_moe_gemm_staged):
@@ -300,6 +305,37 @@ def index_topk_decode(cache: Cache, q_idx, w, K: int, scores, idx, workspace, q_
                                    scores.shape[1], idx.data_ptr(), flags, workspace.data_ptr(),
                                    workspace.numel(), _stream(stream)), "dsa_index_topk_decode", L)
     return scores, idx
+
+
+def index_topk_prefill_workspace(n_q: int, device="cuda"):
+    import torch
+
+    n = lib().dsa_index_topk_prefill_ws(n_q)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def index_topk_prefill(cache: Cache, q_idx, w, q_seq, q_pos, K: int, idx=None, workspace=None,
+                       stream=None, library=None):
+    """dsa_index_topk_prefill: int32 kept positions [n_q, K] of prefill
+    queries (position q_pos[i] of sequence q_seq[i]), no score matrix."""
+    import torch
+
+    L = library or lib()
+    _need(q_idx, torch.bfloat16, "q_idx")
+    _need(w, torch.float32, "w")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(q_pos, torch.int32, "q_pos")
+    n_q, H_idx, _ = q_idx.shape
+    if idx is None:
+        idx = torch.empty((n_q, K), dtype=torch.int32, device=q_idx.device)
+    _need(idx, torch.int32, "idx")
+    if workspace is None:
+        workspace = index_topk_prefill_workspace(n_q, q_idx.device)
+    _check(L.dsa_index_topk_prefill(ctypes.byref(cache.c), q_idx.data_ptr(), w.data_ptr(),
+                                    q_seq.data_ptr(), q_pos.data_ptr(), n_q, H_idx, K,
+                                    idx.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream(stream)), "dsa_index_topk_prefill", L)
+    return idx
 
 
 def check_device_errors(stream=None, library=None) -> int:
@@ -484,13 +520,14 @@ class DecodeStep:
 
 class PrefillStep:
     """Causal prefill of positions pos0 .. pos0+T-1 of sequence `seq` (or, with
-    q_seq / q_pos given, of any queries: q_seq[t], q_pos[t])."""
+    q_seq / q_pos given, of any queries: q_seq[t], q_pos[t]).  fused=True
+    selects with dsa_index_topk_prefill (no score matrix)."""
 
     def __init__(self, cache: Cache, T: int, H: int, K: int, d_v: int, pos0: int = 0,
-                 seq: int = 0, q_seq=None, q_pos=None, device="cuda"):
+                 seq: int = 0, q_seq=None, q_pos=None, device="cuda", fused: bool = False):
         import torch
 
-        self.cache, self.K, self.T = cache, K, T
+        self.cache, self.K, self.T, self.fused = cache, K, T, fused
         if q_pos is None:
             q_pos = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=device)
             q_seq = torch.full((T,), seq, dtype=torch.int32, device=device)
@@ -502,13 +539,24 @@ class PrefillStep:
         self.out = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
         self.ws_topk = topk_workspace(T, ld, K, device)
+        self.ws_fused = index_topk_prefill_workspace(T, device) if fused else None
 
-    def __call__(self, q, q_idx, w, sm_scale: float, stream=None, library=None):
+    def select(self, q_idx, w, stream=None, library=None):
+        """Index score and Top-K of the chunk (self.idx; self.scores too
+        unless fused)."""
         c = self.cache
+        if self.fused:
+            index_topk_prefill(c, q_idx, w, self.q_seq, self.q_pos, self.K, idx=self.idx,
+                               workspace=self.ws_fused, stream=stream, library=library)
+            return
         index_score(c, q_idx, w, DSA_PREFILL, q_seq=self.q_seq, q_pos=self.q_pos,
                     out=self.scores, stream=stream, library=library)
         topk(self.scores, self.K, n_valid=self.n_valid, out=self.idx, workspace=self.ws_topk,
              stream=stream, library=library)
+
+    def __call__(self, q, q_idx, w, sm_scale: float, stream=None, library=None):
+        c = self.cache
+        self.select(q_idx, w, stream=stream, library=library)
         sparse_attn_prefill(c, q, self.q_seq, self.q_pos, self.idx, sm_scale, out=self.out,
                             lse=self.lse, stream=stream, library=library)
         return self.out, self.lse

@@ -535,6 +535,228 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
   }
 }
 
+// ------------------------------------------------- prefill, fused with Top-K
+//
+// Index score and Top-K of prefill rows in one kernel, with no T x T score
+// matrix (web page "Day-0 Adaptation of Trillion-Parameter MoE Models on
+// Domestic GPUs", section 3 item (3): prefill fuses index selection into
+// large-granularity operators).  A persistent grid (two workgroups per CU)
+// walks blocks of four queries, longest first.  Per block: each wave scores
+// its query against key tiles staged in LDS (direct loads, XOR-swizzled
+// rows, as in the prefill kernel above), writing the row of scores into the
+// workgroup's own 128 KB slot of a bounded scratch (it stays in the caches:
+// the slots of all resident workgroups total 64 MB whatever the prefill
+// length); then the wave reads its row back into 128 registers (lane l
+// holds positions 64 i + l) and selects on its own, with no workgroup
+// barrier: the exact K-th largest key by the bitwise search counted with
+// ballots, then one ordered pass that writes the kept positions ascending
+// (equal scores: lower position first).  Rows hold at most 8192 candidates.
+namespace ftk {
+constexpr int kQ = 4;                                 // queries per block (one per wave)
+constexpr int kThreads = kQ * kWave;
+constexpr int kKT = 128;                              // keys per tile
+constexpr int kMaxKeys = 8192;                        // candidates per row at most
+constexpr int kR = kMaxKeys / kWave;                  // keys per lane
+constexpr int kD = 128;
+constexpr int kRowChunks = kD / 8;                    // 16-byte chunks per key row
+constexpr int kTileBytes = kKT * kD * 2;              // 32 KB
+constexpr int kLoads = kTileBytes / (16 * kThreads);  // wave loads per wave per tile
+constexpr int kMaxBlocks = kMaxKeys / 16;             // block-table entries (block_size >= 16)
+constexpr int kSlotFloats = kQ * kMaxKeys;            // scratch floats per workgroup
+constexpr int kMaxGrid = 512;                         // scratch slots
+}  // namespace ftk
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
+
+// Exact Top-K of one row held by one wave (keys k[i] of positions
+// 64 i + lane, 0 = no candidate; n > K candidates): positions written to
+// out[0 .. K-1] ascending, ties to the lower position.
+__device__ __forceinline__ void wave_topk_row(const uint32_t (&k)[ftk::kR], int n, int K,
+                                              int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rounds = (n + kWave - 1) / kWave;  // uniform
+  uint32_t a = 0xffffffffu, o = 0u;
+#pragma unroll
+  for (int i = 0; i < ftk::kR; ++i)
+    if (i < rounds && k[i]) {
+      a &= k[i];
+      o |= k[i];
+    }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    a &= __shfl_xor(a, d);
+    o |= __shfl_xor(o, d);
+  }
+  auto count_ge = [&](uint32_t c) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < ftk::kR; ++i)
+      if (i < rounds) cnt += (uint32_t)__popcll(__ballot(k[i] >= c));
+    return cnt;
+  };
+  uint32_t tau = a, diff = a ^ o;
+  while (diff) {
+    const uint32_t bit = 1u << (31 - __clz(diff));
+    diff &= ~bit;
+    if (count_ge(tau | bit) >= (uint32_t)K) tau |= bit;
+  }
+  const uint32_t gt = tau == 0xffffffffu ? 0u : count_ge(tau + 1u);
+  const uint32_t need = (uint32_t)K - gt;  // keys equal to tau to keep, lowest positions first
+  uint32_t base = 0, eq_seen = 0;
+  const uint64_t below = lanes_below(lane);
+#pragma unroll
+  for (int i = 0; i < ftk::kR; ++i) {
+    if (i < rounds) {
+      const uint64_t meq = __ballot(k[i] == tau);
+      const uint32_t eq_before = eq_seen + (uint32_t)__popcll(meq & below);
+      const bool sel = k[i] > tau || (k[i] == tau && eq_before < need);
+      const uint64_t msel = __ballot(sel);
+      if (sel) out[base + (uint32_t)__popcll(msel & below)] = 64 * i + lane;
+      base += (uint32_t)__popcll(msel);
+      eq_seen += (uint32_t)__popcll(meq);
+    }
+  }
+}
+
+template <int H_IDX>
+__global__ __launch_bounds__(ftk::kThreads, 2) void index_topk_prefill_kernel(
+    const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
+    int max_blocks, int bs, int num_blocks, QueryDesc qd, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, int n_q, int K, int32_t* __restrict__ idx,
+    float* __restrict__ scratch) {
+  using ftk::kD, ftk::kKT, ftk::kLoads, ftk::kQ, ftk::kR, ftk::kRowChunks, ftk::kTileBytes;
+  constexpr int HT = H_IDX / 16, KS = kD / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
+  __shared__ int32_t blk[ftk::kMaxBlocks];
+  __shared__ BlockQueries<kQ> bq;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15, grp = lane >> 4;
+  float* row_scores = scratch + (int64_t)blockIdx.x * ftk::kSlotFloats + wave * ftk::kMaxKeys;
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ktile;
+  const uint64_t row_bytes = (uint64_t)k_stride * 2;
+  const int nqb = (n_q + kQ - 1) / kQ;
+
+  for (int qr = blockIdx.x; qr < nqb; qr += gridDim.x) {
+    const int q0 = (nqb - 1 - qr) * kQ;  // latest positions (usually longest rows) first
+    const int qend = min(q0 + kQ, n_q);
+    __syncthreads();  // the previous block's bq, tiles and block entries are no longer read
+    bq.stage(qd, q0, qend);
+    __syncthreads();
+    const int qi = q0 + wave;
+    const int qrow = qi < qend ? qi : q0;
+    int my_n = qi < qend ? bq.pos[wave] + 1 : 0;  // candidates 0 .. my_n - 1
+    if (my_n > ftk::kMaxKeys) {
+      if (kCheckBounds && lane == 0) raise_error(kErrQuery);
+      my_n = ftk::kMaxKeys;
+    }
+    bf16x8 qa[HT][KS];
+    float wr[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[ht][ks] = as_bf16x8(*(const u32x4*)(q_idx + ((int64_t)qrow * H_IDX + 16 * ht + col) * kD +
+                                                32 * ks + 8 * grp));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[ht][i] = w[(int64_t)qrow * H_IDX + 16 * ht + 4 * grp + i];
+    }
+
+    // ---- scores, one sequence of the block at a time
+    for (int lg = 0; lg < kQ; ++lg) {
+      if (!bq.lead(lg)) continue;  // uniform: LDS data
+      const int b = bq.seq[lg];
+      const int last_pos = min(bq.last_pos(b), ftk::kMaxKeys - 1);
+      const int n_tiles = last_pos / kKT + 1;
+      const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
+      const int qpos = qi < qend && bq.seq[wave] == b ? min(bq.pos[wave], ftk::kMaxKeys - 1) : -1;
+      __syncthreads();  // the previous sequence's tiles and block entries are no longer read
+      for (int e = threadIdx.x; e <= last_pos / bs; e += ftk::kThreads)
+        blk[e] = checked_block(bt_row[e], num_blocks);
+      __syncthreads();
+      // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
+      // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.  Rows
+      // past the last position repeat it (finite data, never stored).
+      auto load_tile = [&](int j, int buf) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          const int bk = kLoads * wave + i;
+          const int slot = kWave * bk + lane;
+          const int r = slot / kRowChunks;
+          const int c = (slot % kRowChunks) ^ (r % kRowChunks);
+          const int pos = min(j * kKT + r, last_pos);
+          const int64_t prow = (int64_t)blk[pos / bs] * bs + pos % bs;
+          const char* src = (const char*)k_idx + (uint64_t)prow * row_bytes + 16 * c;
+          global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * bk));
+        }
+      };
+      load_tile(0, 0);
+      for (int j = 0; j < n_tiles; ++j) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
+        __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
+        if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
+        const uint16_t* kt = ktile[j & 1];
+        const int k0 = j * kKT;
+        const int n = min(kKT, max(0, qpos + 1 - k0));  // keys of this tile the query sees
+        for (int g = 0; 16 * g < n; ++g) {
+          f32x4 acc[HT];
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
+            const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
+          }
+          float sc = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc += wr[ht][i] * relu(acc[ht][i]);
+          sc = wave_sum_xor_16_32(sc);
+          if (grp == 0 && r < n) row_scores[k0 + r] = sc;
+        }
+      }
+    }
+
+    // ---- selection: this wave's row, read back by this wave
+    if (qi < qend) {
+      int32_t* out = idx + (int64_t)qi * K;
+      if (my_n <= K) {
+        for (int r = lane; r < K; r += kWave) out[r] = r < my_n ? r : -1;
+      } else {
+        // the row's scores, stored by this wave's lanes, read back by all of
+        // them: a workgroup-scope release / acquire orders the two (the
+        // workgroup's waves share one L1, written through)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // the row through a buffer resource: the lane offset is one vector
+        // register and each load's offset a scalar constant (128 hoisted
+        // 64-bit addresses would not fit in the registers)
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)row_scores, (short)0, ftk::kMaxKeys * 4, 0x00020000);
+        uint32_t k[kR];
+        const int rounds = (my_n + kWave - 1) / kWave;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          const int p = kWave * i + lane;
+          k[i] = 0u;  // no candidate (float_key of a score is never 0)
+          if (i < rounds) {
+            // entries at or past my_n are stale and masked
+            const float v = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rr, lane * 4, i * kWave * 4, 0));
+            if (p < my_n) k[i] = float_key(v);
+          }
+        }
+        wave_topk_row(k, my_n, K, out);
+      }
+    }
+  }
+}
+
 template <int H_IDX, int D_IDX, bool GMAX>
 dsa_status_t launch_index_score(const dsa_paged_cache_t* c, dsa_phase_t phase,
                                 const uint16_t* q_idx, const float* w, const int32_t* q_seq,
@@ -621,6 +843,54 @@ dsa_status_t launch_index_score_decode_gmax(const dsa_paged_cache_t* c, const ui
 }
 
 }  // namespace dsa
+
+extern "C" size_t dsa_index_topk_prefill_ws(int32_t n_q) {
+  if (n_q < 1) return 0;
+  return (size_t)dsa::ftk::kMaxGrid * dsa::ftk::kSlotFloats * sizeof(float);
+}
+
+extern "C" dsa_status_t dsa_index_topk_prefill(const dsa_paged_cache_t* cache,
+                                               const uint16_t* q_idx, const float* w,
+                                               const int32_t* q_seq, const int32_t* q_pos,
+                                               int32_t n_q, int32_t H_idx, int32_t K, int32_t* idx,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream) {
+  using namespace dsa;
+  dsa_status_t st = check_cache_common(cache);
+  if (st != DSA_OK) return st;
+  if (!cache->k_idx || !q_idx || !w || !q_seq || !q_pos || !idx || !workspace) return DSA_ERR_NULL;
+  if (n_q < 1 || K < 1 || K > 2048 || cache->k_idx_row_stride < cache->d_idx) return DSA_ERR_SHAPE;
+  if (workspace_bytes < dsa_index_topk_prefill_ws(n_q)) return DSA_ERR_WORKSPACE;
+  if (H_idx != 64 || cache->d_idx != 128) return DSA_ERR_UNSUPPORTED;
+  if (cache->k_idx_row_stride % 8 != 0 || cache->block_size % 16 != 0) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(cache->k_idx) || !aligned16(q_idx) || !aligned16(workspace))
+    return DSA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != DSA_OK) return st;
+  static int grid_cache[64] = {0};  // per device: resident workgroups
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int grid = dev < 64 ? grid_cache[dev] : 0;
+  if (grid == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_topk_prefill_kernel<64>,
+                                                     ftk::kThreads, 0) != hipSuccess)
+      return DSA_ERR_HIP;
+    grid = std::max(1, std::min(ftk::kMaxGrid, cus * std::max(1, per_cu)));
+    if (dev < 64) grid_cache[dev] = grid;
+  }
+  const int nqb = (n_q + ftk::kQ - 1) / ftk::kQ;
+  const QueryDesc qd{q_seq, q_pos, cache->seq_lens, cache->n_seq,
+                     (int)std::min<int64_t>((int64_t)cache->max_blocks_per_seq * cache->block_size,
+                                            0x7fffffff),
+                     ftk::kMaxKeys};
+  hipLaunchKernelGGL(index_topk_prefill_kernel<64>, dim3((unsigned)std::min(grid, nqb)),
+                     dim3(ftk::kThreads), 0, stream, cache->k_idx, cache->k_idx_row_stride,
+                     cache->block_table, cache->max_blocks_per_seq, cache->block_size,
+                     cache->num_blocks, qd, q_idx, w, n_q, K, idx, (float*)workspace);
+  return launch_status();
+}
 
 extern "C" size_t dsa_index_score_ws(dsa_phase_t phase, int32_t n_q, int64_t ld) {
   (void)phase;

@@ -142,6 +142,37 @@ def test_index_topk_validation(L):
     assert call(ws_bytes=ws - 1) == 4
 
 
+def test_index_topk_prefill_validation(L):
+    f = L.dsa_index_topk_prefill
+    ws = L.dsa_index_topk_prefill_ws(8192)
+    assert ws == 512 * 4 * 8192 * 4                          # fixed: resident slots, not n_q
+    assert L.dsa_index_topk_prefill_ws(1) == ws
+    assert L.dsa_index_topk_prefill_ws(0) == 0
+
+    def call(c=None, q=FAKE, w=FAKE, q_seq=FAKE, q_pos=FAKE, n_q=100, H=64, K=2048, idx=FAKE,
+             work=FAKE, ws_bytes=ws):
+        c = c or cache()
+        return f(ctypes.byref(c), q, w, q_seq, q_pos, n_q, H, K, idx, work, ws_bytes, None)
+
+    assert call() == 5                                       # well formed: no gfx950 here
+    assert call(c=cache(seq_lens=None)) == 5                 # lengths are not read
+    assert call(q=None) == 1 and call(w=None) == 1 and call(idx=None) == 1
+    assert call(q_seq=None) == 1 and call(q_pos=None) == 1   # per-query arrays required
+    assert call(work=None) == 1
+    assert call(c=cache(k_idx=None)) == 1 and call(c=cache(block_table=None)) == 1
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 100, 64, 2048, FAKE, FAKE, ws, None) == 1
+    assert call(n_q=0) == 2
+    assert call(K=0) == 2 and call(K=2049) == 2
+    assert call(c=cache(k_idx_row_stride=100)) == 2          # stride below width
+    assert call(ws_bytes=ws - 1) == 4
+    assert call(H=32) == 3                                   # indexer shape (64, 128) only
+    assert call(c=cache(d_idx=64, k_idx_row_stride=64)) == 3
+    assert call(c=cache(k_idx_row_stride=132)) == 3          # rows of whole 16-byte chunks
+    assert call(c=cache(block_size=8)) == 3 and call(c=cache(block_size=24)) == 3
+    assert call(c=cache(k_idx=FAKE + 8)) == 3                # 16-byte alignment
+    assert call(q=FAKE + 4) == 3 and call(work=FAKE + 4) == 3
+
+
 def test_attention_validation(L):
     dec = L.dsa_sparse_attn_decode
     pre = L.dsa_sparse_attn_prefill

@@ -14,6 +14,7 @@ import torch
 
 import dsa_synth
 import oracle
+import sparse_attention_long_dsa_amd as dsa
 from tests.helpers import (assert_attention, assert_idx_rows_valid, assert_topk_consistent,
                            attention_margin, gpu_decode, gpu_prefill, oracle_decode_rows, say)
 
@@ -94,4 +95,11 @@ def test_full_prefill():
     rest = np.setdiff1d(np.arange(T), rows)
     pick = np.random.default_rng(3).choice(rest, 256, replace=False)
     assert_topk_consistent(step.scores[pick], step.idx[pick], n_valid[pick], wl.topk)
+    # the fused selection (no score matrix) gives the same kept positions on
+    # every one of the 8192 rows
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    fused = dsa.index_topk_prefill(cache, dc.q_idx, dc.w, step.q_seq, step.q_pos, wl.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, step.idx), "fused prefill selection differs on some row"
+    say("   fused index + Top-K equal on all rows")
     del dc, step

@@ -141,7 +141,31 @@ def check_prefill(wl, pos0=0, T=None, rel=False):
         assert np.array_equal(g_sc[t, :n], sc[t, :n]), f"scores row {t}"
     np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
     mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name, rel=rel)
+    if _fused_applies(wl, pos0 + T):
+        check_fused_prefill(dc, torch.arange(pos0, pos0 + T, dtype=torch.int32, device="cuda"),
+                            torch.zeros(T, dtype=torch.int32, device="cuda"), idx)
     say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
+
+
+def _fused_applies(wl, max_pos_plus_one):
+    """dsa_index_topk_prefill covers the (64, 128) indexer, rows <= 8192."""
+    return wl.H_idx == 64 and wl.d_idx == 128 and max_pos_plus_one <= 8192
+
+
+def check_fused_prefill(dc, q_pos, q_seq, idx_ref, rows=None):
+    """The fused prefill selection (no score matrix) on the same queries: the
+    kept positions equal the oracle's, exactly."""
+    wl = dc.wl
+    T = q_pos.shape[0]
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    if rows is None:
+        q_idx, w = dc.q_idx[q_pos.long()].contiguous(), dc.w[q_pos.long()].contiguous()
+    else:
+        q_idx, w = rows
+    got = dsa.index_topk_prefill(cache, q_idx, w, q_seq, q_pos, wl.topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), idx_ref, err_msg="fused prefill selection")
+    say(f"   fused index + Top-K: {T} rows exact")
 
 
 def test_latent_prefill():
@@ -392,6 +416,9 @@ def _check_queries(wl, q_seq, q_pos, sm_scale=None, rel=False):
         assert np.array_equal(g_sc[i, :q_pos[i] + 1], sc[i, :q_pos[i] + 1]), f"scores row {i}"
     np.testing.assert_array_equal(step.idx.cpu().numpy(), idx)
     mx, mn = assert_attention(step.out, step.lse, out, lse, wl.name, rel=rel)
+    if _fused_applies(wl, int(q_pos.max()) + 1):
+        check_fused_prefill(dc, torch.from_numpy(q_pos).cuda(), torch.from_numpy(q_seq).cuda(),
+                            idx, rows=(_dev_bf16(q_idx), torch.from_numpy(w).cuda()))
     say(f"   ok: max|err| {mx:.2e} mean|err| {mn:.2e}")
     return dc, step, (sc, idx, out, lse)
 
@@ -684,3 +711,56 @@ def test_incremental_decode_eight_steps():
         np.testing.assert_array_equal(st.idx.cpu().numpy(), idx, err_msg=f"step {s_}")
         mx, mn = assert_attention(st.out, st.lse, out, lse, f"step {s_}")
         say(f"   step {s_}: lengths {lens.tolist()}: Top-K exact, attention max|err| {mx:.2e}")
+
+
+def test_fused_prefill_mixed_blocks_short_rows_and_reuse():
+    """The fused prefill selection over queries that interleave two
+    sequences inside every 4-query block, rows shorter than K (all kept, -1
+    padded), the last position allowed (8191), and a second call on the same
+    workspace."""
+    wl = dsa_synth.latent("fused_mix", "decode", [8192, 3000], seed=61, topk=512)
+    rng = np.random.default_rng(7)
+    pos0 = np.concatenate([rng.integers(0, 8192, 120), [8191, 0, 1, 511, 512, 513]])
+    pos1 = rng.integers(0, 3000, 126)
+    q_seq = np.empty(252, np.int32)
+    q_pos = np.empty(252, np.int32)
+    q_seq[0::2], q_pos[0::2] = 0, pos0
+    q_seq[1::2], q_pos[1::2] = 1, pos1
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    _, q_idx, w = dsa_synth.host_query_rows(wl, 0, len(q_seq))
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos,
+                            ld=8192)
+    idx = oracle.topk(sc, q_pos + 1, wl.topk)
+    say(f"[fused prefill] {len(q_seq)} queries over 2 sequences, K={wl.topk}")
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    ws = dsa.index_topk_prefill_workspace(len(q_seq))
+    args = (cache, _dev_bf16(q_idx), torch.from_numpy(w).cuda(), torch.from_numpy(q_seq).cuda(),
+            torch.from_numpy(q_pos).cuda(), wl.topk)
+    for rep in range(2):
+        got = dsa.index_topk_prefill(*args, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), idx, err_msg=f"call {rep}")
+    say("   exact on both calls")
+
+
+def test_fused_prefill_debug_build_flags_positions_past_8192():
+    D = dsa.debug_lib()
+    wl = dsa_synth.latent("fused_dbg", "decode", [9000], seed=62, topk=64)
+    dc = dsa_synth.device_case(wl)
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    assert dsa.check_device_errors(library=D) == 0
+    # eight queries of the one sequence (the decode case has a single query row)
+    q8 = dc.q_idx[:1].repeat(8, 1, 1).contiguous()
+    w8 = dc.w[:1].repeat(8, 1).contiguous()
+    q_seq = torch.zeros(8, dtype=torch.int32, device="cuda")
+    ok = torch.arange(8184, 8192, dtype=torch.int32, device="cuda")  # up to 8192 candidates
+    good = dsa.index_topk_prefill(cache, q8, w8, q_seq, ok, wl.topk, library=D)
+    assert dsa.check_device_errors(library=D) == 0
+    rel = dsa.index_topk_prefill(cache, q8, w8, q_seq, ok, wl.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(good, rel)
+    bad = torch.arange(8190, 8198, dtype=torch.int32, device="cuda")  # 8193 .. 8198 candidates
+    dsa.index_topk_prefill(cache, q8, w8, q_seq, bad, wl.topk, library=D)
+    assert dsa.check_device_errors(library=D) == 7
+    assert dsa.check_device_errors(library=D) == 0
