@@ -275,18 +275,33 @@ def bench_prefill(timer, reps, warmup, log):
              lambda: dsa.sparse_attn_prefill(cache, dc.q, st.q_seq, st.q_pos, st.idx,
                                              wl.sm_scale, out=st.out, lse=st.lse)]
     r = timer.run(calls, reps, warmup)
+    # the same step with the fused selection (index score + Top-K, no score matrix)
+    stf = dsa.PrefillStep(cache, T, wl.H, wl.topk, wl.d_v, fused=True)
+    rf = timer.run([lambda: stf.select(dc.q_idx, dc.w),
+                    lambda: dsa.sparse_attn_prefill(cache, dc.q, stf.q_seq, stf.q_pos, stf.idx,
+                                                    wl.sm_scale, out=stf.out, lse=stf.lse)],
+                   reps, warmup)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(stf.idx, st.idx))
     fi, fa = prefill_flops(wl)
-    ms = r["median_ms"]
-    parts = r["per_call_ms"]
+    ms, msf = r["median_ms"], rf["median_ms"]
+    parts, pf = r["per_call_ms"], rf["per_call_ms"]
     peak = MFMA_BF16_CLOCK_PEAK_TF
     res = {
-        "workload": wl.name, "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "ms_per_step": round(ms, 4), "reps": reps, "ms_min": round(r["min_ms"], 4),
-        "index_ms": round(parts[0], 4), "topk_ms": round(parts[1], 4),
-        "attn_ms": round(parts[2], 4), "flops": fi + fa, "mfma_peak_tflops": peak,
-        "mfma_util": round((fi + fa) / (ms * 1e-3) / 1e12 / peak, 4),
-        "attn_mfma_util": round(fa / (parts[2] * 1e-3) / 1e12 / peak, 4),
-        "index_mfma_util": round(fi / (parts[0] * 1e-3) / 1e12 / peak, 4)}
+        "workload": wl.name, "tokens_per_s": round(T / (msf * 1e-3), 1),
+        "ms_per_step": round(msf, 4), "reps": reps, "ms_min": round(rf["min_ms"], 4),
+        "select_ms": round(pf[0], 4), "attn_ms": round(pf[1], 4),
+        "select_equal_to_separate": same,
+        "flops": fi + fa, "mfma_peak_tflops": peak,
+        "mfma_util": round((fi + fa) / (msf * 1e-3) / 1e12 / peak, 4),
+        "attn_mfma_util": round(fa / (pf[1] * 1e-3) / 1e12 / peak, 4),
+        "select_index_mfma_util": round(fi / (pf[0] * 1e-3) / 1e12 / peak, 4),
+        "separate": {"ms_per_step": round(ms, 4), "ms_min": round(r["min_ms"], 4),
+                     "index_ms": round(parts[0], 4), "topk_ms": round(parts[1], 4),
+                     "attn_ms": round(parts[2], 4),
+                     "index_mfma_util": round(fi / (parts[0] * 1e-3) / 1e12 / peak, 4),
+                     "score_matrix_bytes": int(st.scores.numel()) * 4}}
+    del stf
     # the cache write of the whole sequence: its own rows written back from a
     # contiguous copy (gathered untimed), so the pools end up unchanged
     stream = torch.cuda.current_stream()

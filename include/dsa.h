@@ -197,8 +197,9 @@ dsa_status_t dsa_index_topk_decode(const dsa_paged_cache_t *cache, const uint16_
                                    int64_t ld, int32_t *idx, int32_t flags, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes dsa_index_topk_prefill needs: a fixed 64 MiB (the scratch
- * slots of the resident workgroups, whatever n_q), or 0 for n_q < 1. */
+/* Workspace bytes dsa_index_topk_prefill needs: one 512 KB score slot per
+ * workgroup of its persistent grid, min(256, ceil(n_q / 16)) slots (at most
+ * 128 MiB whatever n_q), or 0 for n_q < 1. */
 size_t dsa_index_topk_prefill_ws(int32_t n_q);
 
 /* Index score and Top-K fused for prefill rows (page 1, section 3 item (3):
@@ -207,16 +208,17 @@ size_t dsa_index_topk_prefill_ws(int32_t n_q);
  * dsa_index_score (DSA_PREFILL) followed by dsa_topk would give for query i
  * (position q_pos[i] of sequence q_seq[i], candidates 0 .. q_pos[i];
  * ascending, ties to the lower position, -1 padded), and no scores are
- * written.  A persistent grid of workgroups takes blocks of four queries;
- * each query's scores pass through the workgroup's slot of the workspace
- * (128 KB a workgroup, re-used block after block, so it stays in the
- * caches).  Rows are limited to 8192 candidates: q_pos[i] < 8192 (device
- * data: a debug build reports a larger position, a release build selects
- * among the first 8192); chunk longer prefills through the two separate
- * calls.  Indexer shape (64, 128) only; block_size a multiple of 16;
- * 1 <= K <= 2048.  q_seq and q_pos are required.  Workspace:
- * dsa_index_topk_prefill_ws(n_q) bytes, 16-byte aligned, no
- * initialisation. */
+ * written.  A persistent grid (one workgroup per CU) takes blocks of 16
+ * queries; the scores of a block's rows pass through the workgroup's slot
+ * of the workspace and are selected there (a row with at most K
+ * candidates keeps them all and is not scored).  Rows are limited to 8192
+ * candidates: q_pos[i] < 8192 (device data: a debug build reports a larger
+ * position, a release build selects among the first 8192); chunk longer
+ * prefills through the two separate calls.  Indexer shape (64, 128) only;
+ * block_size a multiple of 16; 1 <= K <= 2048.  q_seq and q_pos are
+ * required.  Workspace: dsa_index_topk_prefill_ws(n_q) bytes, 16-byte
+ * aligned, no initialisation; calls that share a workspace must not
+ * overlap. */
 dsa_status_t dsa_index_topk_prefill(const dsa_paged_cache_t *cache, const uint16_t *q_idx,
                                     const float *w, const int32_t *q_seq, const int32_t *q_pos,
                                     int32_t n_q, int32_t H_idx, int32_t K, int32_t *idx,

@@ -204,6 +204,11 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    """Size in bytes of a workspace tensor of any dtype."""
+    return t.numel() * t.element_size()
+
+
 def _stream(stream=None):
     import torch
 
@@ -303,7 +308,7 @@ def index_topk_decode(cache: Cache, q_idx, w, K: int, scores, idx, workspace, q_
     _check(L.dsa_index_topk_decode(ctypes.byref(cache.c), q_idx.data_ptr(), w.data_ptr(),
                                    _ptr(q_seq), _ptr(q_pos), n_q, H_idx, K, scores.data_ptr(),
                                    scores.shape[1], idx.data_ptr(), flags, workspace.data_ptr(),
-                                   workspace.numel(), _stream(stream)), "dsa_index_topk_decode", L)
+                                   _nbytes(workspace), _stream(stream)), "dsa_index_topk_decode", L)
     return scores, idx
 
 
@@ -333,7 +338,7 @@ def index_topk_prefill(cache: Cache, q_idx, w, q_seq, q_pos, K: int, idx=None, w
         workspace = index_topk_prefill_workspace(n_q, q_idx.device)
     _check(L.dsa_index_topk_prefill(ctypes.byref(cache.c), q_idx.data_ptr(), w.data_ptr(),
                                     q_seq.data_ptr(), q_pos.data_ptr(), n_q, H_idx, K,
-                                    idx.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    idx.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
                                     _stream(stream)), "dsa_index_topk_prefill", L)
     return idx
 
@@ -368,7 +373,7 @@ def topk(scores, K: int, n_valid=None, causal_base: int = 0, out=None, workspace
     if workspace is None:
         workspace = topk_workspace(n_q, ld, K, scores.device)
     _check(L.dsa_topk(scores.data_ptr(), ld, n_q, K, _ptr(n_valid), causal_base,
-                      out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)),
+                      out.data_ptr(), workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
            "dsa_topk", L)
     return out
 
@@ -399,7 +404,7 @@ def sparse_attn_decode(cache: Cache, q, idx, sm_scale: float, out=None, lse=None
         workspace = decode_workspace(B, H, K, d_v, q.device)
     _check(L.dsa_sparse_attn_decode(ctypes.byref(cache.c), q.data_ptr(), idx.data_ptr(), B, H,
                                     K, float(sm_scale), out.data_ptr(), _ptr(lse),
-                                    workspace.data_ptr(), workspace.numel(), _stream(stream)),
+                                    workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
            "dsa_sparse_attn_decode", L)
     return out, lse
 
@@ -702,7 +707,7 @@ class MoeStaged:
         _need(out, torch.float32, "y")
         _check(L.dsa_moe_gemm_staged(ctypes.byref(experts.w), x.data_ptr(), expert_ids.data_ptr(),
                                      row_offsets.data_ptr(), n_act, M, max_rows, out.data_ptr(),
-                                     self.workspace.data_ptr(), self.workspace.numel(),
+                                     self.workspace.data_ptr(), _nbytes(self.workspace),
                                      _stream(stream), ctypes.c_void_p(self.conv_stream.cuda_stream),
                                      self._events), "dsa_moe_gemm_staged", L)
         return out

@@ -425,6 +425,103 @@ constexpr int kD = 128;
 constexpr int kRowChunks = kD / 8;                    // 16-byte chunks per key row
 constexpr int kTileBytes = kKT * kD * 2;              // 32 KB
 constexpr int kLoads = kTileBytes / (16 * kThreads);  // wave loads per wave per tile
+
+// LDS of one workgroup: two key tiles and the physical rows of the chunk.
+struct Stage {
+  __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
+  int32_t prow[kChunk * kKT];
+};
+
+// This wave's query as the A operand (head 16 ht + col, dims 32 ks + 8 grp
+// ..) and the weights of the heads in this lane's result rows.
+template <int H_IDX>
+struct QueryRegs {
+  bf16x8 qa[H_IDX / 16][kD / 32];
+  float wr[H_IDX / 16][4];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ q_idx,
+                                       const float* __restrict__ w, int qr, int col, int grp) {
+#pragma unroll
+    for (int ht = 0; ht < H_IDX / 16; ++ht) {
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks)
+        qa[ht][ks] = as_bf16x8(*(const u32x4*)(q_idx + ((int64_t)qr * H_IDX + 16 * ht + col) * kD +
+                                                32 * ks + 8 * grp));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[ht][i] = w[(int64_t)qr * H_IDX + 16 * ht + 4 * grp + i];
+    }
+  }
+};
+
+// Scores of one sequence's keys at positions k_begin .. k_end - 1 (at most
+// kChunk tiles) against every wave's query: the wave whose query sits at
+// position qpos of this sequence (-1: none) writes the score of position p
+// (p <= qpos) to out[p].  All waves of the workgroup call it together (it
+// holds workgroup barriers); on return the tiles may be overwritten.
+template <int H_IDX>
+__device__ __forceinline__ void score_sequence(
+    Stage& st, const uint16_t* __restrict__ k_idx, uint64_t row_bytes,
+    const int32_t* __restrict__ bt_row, int bs, int num_blocks, int k_begin, int k_end, int qpos,
+    const QueryRegs<H_IDX>& q, float* __restrict__ out, int tid) {
+  constexpr int HT = H_IDX / 16, KS = kD / 32;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
+  __syncthreads();  // the previous sequence's tiles and rows are no longer read
+  // physical rows of the chunk's keys; slots past k_end repeat the first
+  // key (finite data, never stored)
+  for (int r = tid; r < n_tiles * kKT; r += kThreads) {
+    const int pos = k_begin + r;
+    st.prow[r] = (int32_t)paged_row(bt_row, bs, pos < k_end ? pos : k_begin, num_blocks);
+  }
+  __syncthreads();  // prow
+
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)st.ktile;
+  // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
+  // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.
+  auto load_tile = [&](int j, int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int blk = kLoads * wave + i;
+      const int slot = kWave * blk + lane;
+      const int r = slot / kRowChunks;
+      const int c = (slot % kRowChunks) ^ (r % kRowChunks);
+      const char* src =
+          (const char*)k_idx + (uint64_t)(uint32_t)st.prow[j * kKT + r] * row_bytes + 16 * c;
+      global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * blk));
+    }
+  };
+  load_tile(0, 0);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
+    __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
+    if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
+    const uint16_t* kt = st.ktile[j & 1];
+    const int k0 = k_begin + j * kKT;
+    const int n = min(kKT, max(0, qpos + 1 - k0));  // keys of this tile the query sees
+    for (int g = 0; 16 * g < n; ++g) {
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
+        const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(q.qa[ht][ks], kb, acc[ht]);
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc += q.wr[ht][i] * relu(acc[ht][i]);
+      sc = wave_sum_xor_16_32(sc);
+      if (grp == 0 && r < n) out[k0 + r] = sc;
+    }
+  }
+}
 }  // namespace pf
 
 template <int H_IDX>
@@ -432,10 +529,8 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, int num_blocks, QueryDesc qd, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, int n_q, float* __restrict__ scores, int64_t ld) {
-  using pf::kChunk, pf::kD, pf::kKT, pf::kLoads, pf::kQB, pf::kRowChunks, pf::kTileBytes;
-  constexpr int HT = H_IDX / 16, KS = kD / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
-  __shared__ int32_t prow[kChunk * kKT];
+  using pf::kChunk, pf::kKT, pf::kQB;
+  __shared__ pf::Stage st;
   __shared__ BlockQueries<kQB> bq;
 
   // the query blocks of the latest positions (usually the longest rows)
@@ -447,91 +542,22 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int col = lane & 15, grp = lane >> 4;
-
-  // this wave's query: q as the A operand (head 16 ht + col, dims
-  // 32 ks + 8 grp ..), the weights of the heads in this lane's result rows
   const int qi = q0 + wave;
-  const int qr = qi < qend ? qi : q0;
-  bf16x8 qa[HT][KS];
-  float wr[HT][4];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qa[ht][ks] = as_bf16x8(
-          *(const u32x4*)(q_idx + ((int64_t)qr * H_IDX + 16 * ht + col) * kD + 32 * ks + 8 * grp));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wr[ht][i] = w[(int64_t)qr * H_IDX + 16 * ht + 4 * grp + i];
-  }
+  pf::QueryRegs<H_IDX> q;
+  q.load(q_idx, w, qi < qend ? qi : q0, lane & 15, lane >> 4);
   __syncthreads();  // bq
 
-  const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ktile;
-  const uint64_t row_bytes = (uint64_t)k_stride * 2;
   for (int lg = 0; lg < kQB; ++lg) {
     if (!bq.lead(lg)) continue;  // uniform: LDS data
     const int b = bq.seq[lg];
     const int last_pos = bq.last_pos(b);
     if (k_begin > last_pos) continue;
-    const int k_end = min(k_begin + kChunk * kKT, last_pos + 1);
-    const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
-    const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
     // this wave's query position if it belongs to sequence b (wave-uniform)
     const int qpos = qi < qend && bq.seq[wave] == b ? bq.pos[wave] : -1;
-
-    __syncthreads();  // the previous sequence's tiles and rows are no longer read
-    // physical rows of the chunk's keys; slots past k_end repeat the first
-    // key (finite data, never stored)
-    for (int r = threadIdx.x; r < n_tiles * kKT; r += pf::kThreads) {
-      const int pos = k_begin + r;
-      prow[r] = (int32_t)paged_row(bt_row, bs, pos < k_end ? pos : k_begin, num_blocks);
-    }
-    __syncthreads();  // prow
-
-    // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
-    // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.
-    auto load_tile = [&](int j, int buf) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int blk = kLoads * wave + i;
-        const int slot = kWave * blk + lane;
-        const int r = slot / kRowChunks;
-        const int c = (slot % kRowChunks) ^ (r % kRowChunks);
-        const char* src =
-            (const char*)k_idx + (uint64_t)(uint32_t)prow[j * kKT + r] * row_bytes + 16 * c;
-        global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * blk));
-      }
-    };
-    load_tile(0, 0);
-
-    for (int j = 0; j < n_tiles; ++j) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
-      __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
-      if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
-      const uint16_t* kt = ktile[j & 1];
-      const int k0 = k_begin + j * kKT;
-      const int n = min(kKT, max(0, qpos + 1 - k0));  // keys of this tile the query sees
-      for (int g = 0; 16 * g < n; ++g) {
-        f32x4 acc[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
-          const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
-        }
-        float sc = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc += wr[ht][i] * relu(acc[ht][i]);
-        sc = wave_sum_xor_16_32(sc);
-        if (grp == 0 && r < n) scores[(int64_t)qi * ld + k0 + r] = sc;
-      }
-    }
+    pf::score_sequence<H_IDX>(st, k_idx, (uint64_t)k_stride * 2,
+                              block_table + (int64_t)b * max_blocks, bs, num_blocks, k_begin,
+                              min(k_begin + kChunk * kKT, last_pos + 1), qpos, q,
+                              scores + (int64_t)qi * ld, threadIdx.x);
   }
 }
 
@@ -540,45 +566,91 @@ __global__ __launch_bounds__(pf::kThreads, 1) void index_score_prefill_kernel(
 // Index score and Top-K of prefill rows in one kernel, with no T x T score
 // matrix (web page "Day-0 Adaptation of Trillion-Parameter MoE Models on
 // Domestic GPUs", section 3 item (3): prefill fuses index selection into
-// large-granularity operators).  A persistent grid (two workgroups per CU)
-// walks blocks of four queries, longest first.  Per block: each wave scores
-// its query against key tiles staged in LDS (direct loads, XOR-swizzled
-// rows, as in the prefill kernel above), writing the row of scores into the
-// workgroup's own 128 KB slot of a bounded scratch (it stays in the caches:
-// the slots of all resident workgroups total 64 MB whatever the prefill
-// length); then the wave reads its row back into 128 registers (lane l
-// holds positions 64 i + l) and selects on its own, with no workgroup
-// barrier: the exact K-th largest key by the bitwise search counted with
-// ballots, then one ordered pass that writes the kept positions ascending
-// (equal scores: lower position first).  Rows hold at most 8192 candidates.
+// large-granularity operators).  A persistent grid, one workgroup per CU,
+// walks blocks of 16 queries.  Per block: the queries with more than K
+// candidates are scored exactly as by the prefill kernel above (a row with
+// at most K candidates keeps all of them whatever its scores, so it is not
+// scored), each wave's row of scores going to its row of the workgroup's
+// 512 KB slot of a bounded scratch (the slots of all resident workgroups
+// total 128 MB whatever the prefill length); then pairs of waves select:
+// the two waves of a pair split a row in halves (64 keys a lane), find the
+// exact K-th largest key by the bitwise search, each step's two counts
+// exchanged through LDS at a workgroup barrier (once at most 512 keys are
+// still open, each wave moves its open keys into an LDS list and counts
+// only those), and write the kept positions ascending (equal scores: lower
+// position first).  Rows hold at most 8192 candidates.
 namespace ftk {
-constexpr int kQ = 4;                                 // queries per block (one per wave)
-constexpr int kThreads = kQ * kWave;
-constexpr int kKT = 128;                              // keys per tile
-constexpr int kMaxKeys = 8192;                        // candidates per row at most
-constexpr int kR = kMaxKeys / kWave;                  // keys per lane
-constexpr int kD = 128;
-constexpr int kRowChunks = kD / 8;                    // 16-byte chunks per key row
-constexpr int kTileBytes = kKT * kD * 2;              // 32 KB
-constexpr int kLoads = kTileBytes / (16 * kThreads);  // wave loads per wave per tile
-constexpr int kMaxBlocks = kMaxKeys / 16;             // block-table entries (block_size >= 16)
-constexpr int kSlotFloats = kQ * kMaxKeys;            // scratch floats per workgroup
-constexpr int kMaxGrid = 512;                         // scratch slots
+constexpr int kQ = pf::kQB;                     // queries per block (one per wave)
+constexpr int kMaxKeys = pf::kChunk * pf::kKT;  // candidates per row at most (8192)
+constexpr int kHalf = kMaxKeys / 2;             // keys of a row per wave of a pair
+constexpr int kR = kHalf / kWave;               // keys per lane (64)
+constexpr int kSlotFloats = kQ * kMaxKeys;      // scratch floats per workgroup (512 KB)
+constexpr int kMaxGrid = 256;                   // scratch slots
+constexpr int kOpen = 512;                      // open keys listed per wave (LDS)
+
+// Counts exchanged between the two waves of a pair (indexed by wave).
+struct PairCounts {
+  uint32_t a[kQ], o[kQ], c[2][kQ], gt[kQ], eq[kQ], steps[kQ];
+};
 }  // namespace ftk
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-// Exact Top-K of one row held by one wave (keys k[i] of positions
-// 64 i + lane, 0 = no candidate; n > K candidates): positions written to
-// out[0 .. K-1] ascending, ties to the lower position.
-__device__ __forceinline__ void wave_topk_row(const uint32_t (&k)[ftk::kR], int n, int K,
-                                              int32_t* __restrict__ out) {
+// Set bits of the wave mask m in the lanes below this one.
+__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// A value every lane of the wave holds alike, made visibly wave-uniform (a
+// scalar register) for the compiler: values read from LDS or passed to an
+// out-of-line function otherwise count as per-lane.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const uint64_t u = (uint64_t)p;
+  return (T*)(((uint64_t)uni((uint32_t)(u >> 32)) << 32) | uni((uint32_t)u));
+}
+
+// Exact Top-K of one row held by a pair of waves (waves 2p and 2p + 1):
+// wave h of the pair holds the keys of candidates pos0 + 64 i + lane in k[i]
+// (0 = no candidate; i < rounds) and writes its kept positions into out.
+// Every wave of the workgroup calls this together: the barriers it holds
+// are the same in number in every wave (2, one per search step of the pair
+// with the most bits to decide, then 1).  `active` (the same in both waves of a pair)
+// is false when the pair has no row with more than K candidates; such a
+// pair only takes part in the barriers; n is the row's candidate count.
+//
+// The K-th largest key tau is found one bit at a time from the top; both
+// waves track, as pair totals, A (keys whose bits above the current one
+// exceed tau's: kept) and U (keys whose bits above it equal tau's: still
+// open).  Once U <= kOpen, each wave moves its open keys into its own LDS
+// list and the remaining bits count only those (at most 8 a lane).
+__device__ __forceinline__ void pair_topk_row(const uint32_t (&k)[ftk::kR], int rounds,
+                                              bool active, int n, int K, int pos0,
+                                              int32_t* __restrict__ out, ftk::PairCounts& x,
+                                              uint32_t* __restrict__ open_list) {
+  using ftk::kOpen, ftk::kR;
+  constexpr int kOL = kOpen / kWave;  // open keys per lane
   const int lane = threadIdx.x & (kWave - 1);
-  const int rounds = (n + kWave - 1) / kWave;  // uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int mate = wave ^ 1;
+  // keys >= c among k (chunks of 8: keys past `rounds` are 0 and never
+  // reach c >= 1)
+  auto count_ge = [&](uint32_t c) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i0 = 0; i0 < kR; i0 += 8)
+      if (i0 < rounds) {
+#pragma unroll
+        for (int i = i0; i < i0 + 8; ++i) cnt += (uint32_t)__popcll(__ballot(k[i] >= c));
+      }
+    return cnt;
+  };
+  // bits where the row's keys differ (AND / OR over both halves)
   uint32_t a = 0xffffffffu, o = 0u;
 #pragma unroll
-  for (int i = 0; i < ftk::kR; ++i)
-    if (i < rounds && k[i]) {
+  for (int i = 0; i < kR; ++i)
+    if (k[i]) {
       a &= k[i];
       o |= k[i];
     }
@@ -587,172 +659,266 @@ __device__ __forceinline__ void wave_topk_row(const uint32_t (&k)[ftk::kR], int 
     a &= __shfl_xor(a, d);
     o |= __shfl_xor(o, d);
   }
-  auto count_ge = [&](uint32_t c) {
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < ftk::kR; ++i)
-      if (i < rounds) cnt += (uint32_t)__popcll(__ballot(k[i] >= c));
-    return cnt;
-  };
-  uint32_t tau = a, diff = a ^ o;
-  while (diff) {
-    const uint32_t bit = 1u << (31 - __clz(diff));
-    diff &= ~bit;
-    if (count_ge(tau | bit) >= (uint32_t)K) tau |= bit;
+  a = uni(a);
+  o = uni(o);
+  if (lane == 0) {
+    x.a[wave] = a;
+    x.o[wave] = o;
   }
-  const uint32_t gt = tau == 0xffffffffu ? 0u : count_ge(tau + 1u);
-  const uint32_t need = (uint32_t)K - gt;  // keys equal to tau to keep, lowest positions first
-  uint32_t base = 0, eq_seen = 0;
-  const uint64_t below = lanes_below(lane);
+  __syncthreads();
+  a &= uni(x.a[mate]);
+  o |= uni(x.o[mate]);
+  uint32_t tau = a;  // bits not in diff are those of every key
+  const uint32_t diff = active ? a ^ o : 0u;
+  // search steps: one per bit of diff, as many in every wave as the pair
+  // with the most needs
+  if (lane == 0) x.steps[wave] = (uint32_t)__popc(diff);
+  __syncthreads();
+  uint32_t n_steps = 0;
 #pragma unroll
-  for (int i = 0; i < ftk::kR; ++i) {
-    if (i < rounds) {
-      const uint64_t meq = __ballot(k[i] == tau);
-      const uint32_t eq_before = eq_seen + (uint32_t)__popcll(meq & below);
-      const bool sel = k[i] > tau || (k[i] == tau && eq_before < need);
-      const uint64_t msel = __ballot(sel);
-      if (sel) out[base + (uint32_t)__popcll(msel & below)] = 64 * i + lane;
-      base += (uint32_t)__popcll(msel);
-      eq_seen += (uint32_t)__popcll(meq);
+  for (int v = 0; v < ftk::kQ; ++v) n_steps = max(n_steps, uni(x.steps[v]));
+  uint32_t kept = 0, open = (uint32_t)n;  // A and U (pair totals)
+  // the lists hold the keys open when they were made: those kept since are
+  // in them too, those kept before are not
+  uint32_t kept_listed = 0;
+  bool listed = false;  // the same in both waves of the pair
+  uint32_t u[kOL];
+#pragma unroll
+  for (int j = 0; j < kOL; ++j) u[j] = 0u;
+  int list_len = 0;
+  uint32_t rest = diff;  // bits still to decide, highest first
+  for (uint32_t step = 0; step < n_steps; ++step) {
+    const int bit = rest ? 31 - __clz(rest) : 0;
+    const uint32_t b = rest ? 1u << bit : 0u;
+    rest &= ~b;
+    const bool test = b != 0u;  // the same in both waves of the pair
+    if (test && !listed && open <= (uint32_t)kOpen) {
+      // this wave's open keys (bits above `bit` equal to tau's) into its
+      // list; the order does not matter for counting
+      listed = true;
+      kept_listed = kept;
+#pragma unroll
+      for (int i0 = 0; i0 < kR; i0 += 8)
+        if (i0 < rounds) {
+#pragma unroll
+          for (int i = i0; i < i0 + 8; ++i) {
+            const bool op = k[i] != 0u && ((k[i] ^ tau) >> bit) <= 1u;
+            const uint64_t m = __ballot(op);
+            const int at = list_len + (int)bits_below(m);
+            if (op && at < kOpen) open_list[at] = k[i];  // at < kOpen: open <= kOpen
+            list_len += __popcll(m);
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < kOL; ++j)
+        u[j] = kWave * j + lane < list_len ? open_list[kWave * j + lane] : 0u;
+    }
+    // keys of this wave (of its list, once listed) >= tau | b: the kept
+    // ones (since listing) and the open ones with bit b set
+    uint32_t c = 0;
+    if (test) {
+      if (listed) {
+#pragma unroll
+        for (int j = 0; j < kOL; ++j)
+          if (kWave * j < list_len) c += (uint32_t)__popcll(__ballot(u[j] >= (tau | b)));
+      } else {
+        c = count_ge(tau | b);
+      }
+    }
+    if (lane == 0) x.c[step & 1][wave] = c;
+    __syncthreads();
+    if (test) {
+      c += uni(x.c[step & 1][mate]);
+      const uint32_t open1 = c - (kept - kept_listed);  // open keys with bit b set
+      if (kept + open1 >= (uint32_t)K) {
+        tau |= b;
+        open = open1;
+      } else {
+        kept += open1;
+        open -= open1;
+      }
     }
   }
+  // keys above tau and equal to tau in this half
+  uint32_t gt = 0, eq = 0;
+  if (active) {
+#pragma unroll
+    for (int i0 = 0; i0 < kR; i0 += 8)
+      if (i0 < rounds) {
+#pragma unroll
+        for (int i = i0; i < i0 + 8; ++i) {
+          gt += (uint32_t)__popcll(__ballot(k[i] > tau));
+          eq += (uint32_t)__popcll(__ballot(k[i] == tau));
+        }
+      }
+  }
+  if (lane == 0) {
+    x.gt[wave] = gt;
+    x.eq[wave] = eq;
+  }
+  __syncthreads();
+  if (!active) return;
+  const uint32_t gt_mate = uni(x.gt[mate]);
+  const uint32_t need = (uint32_t)K - (gt + gt_mate);  // keys equal to tau to keep
+  // the second half starts after everything the first half keeps
+  uint32_t base = 0, eq_seen = 0;
+  if (wave & 1) {
+    eq_seen = uni(x.eq[mate]);
+    base = gt_mate + min(need, eq_seen);
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < kR; i0 += 8)
+    if (i0 < rounds) {
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) {
+        const uint64_t meq = __ballot(k[i] == tau);
+        const uint32_t eq_before = eq_seen + bits_below(meq);
+        const bool sel = k[i] > tau || (k[i] == tau && eq_before < need);
+        const uint64_t msel = __ballot(sel);
+        const uint32_t slot = base + bits_below(msel);
+        if (sel && slot < (uint32_t)K) out[slot] = pos0 + kWave * i + lane;
+        base += (uint32_t)__popcll(msel);
+        eq_seen += (uint32_t)__popcll(meq);
+      }
+    }
+}
+
+// One wave's half of a row for pair_topk_row: its `mine` scores (from
+// `row`, positions pos0 ..) read back as keys, then the selection.  Kept
+// out of line: its registers are allocated apart from the scoring loop's,
+// which otherwise spills (and each reload waits for the tile prefetch).
+__device__ __attribute__((noinline)) void select_pair_row(const float* row_arg, int mine_arg,
+                                                          int active_arg, int n_arg, int K_arg,
+                                                          int pos0_arg, int32_t* out_arg) {
+  __shared__ ftk::PairCounts x;
+  __shared__ uint32_t open_lists[ftk::kQ][ftk::kOpen];
+  // every argument is the same in all lanes of the wave
+  const float* row = uni_ptr(row_arg);
+  int32_t* out = uni_ptr(out_arg);
+  const int mine = (int)uni(mine_arg), n = (int)uni(n_arg), K = (int)uni(K_arg);
+  const int pos0 = (int)uni(pos0_arg);
+  const bool active = uni(active_arg) != 0u;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int rounds = active ? (mine + kWave - 1) / kWave : 0;
+  uint32_t k[ftk::kR];
+  // the row through a buffer resource: the lane offset is one vector
+  // register and each load's offset a scalar constant
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, ftk::kHalf * 4, 0x00020000);
+  // every load is issued (a conditional one would wait at its branch);
+  // they stay inside the row's half, entries past `mine` are stale and
+  // masked (0 = no candidate: float_key of a score is never 0)
+  // (the raw bits land in k first, so all 64 loads fly at once)
+#pragma unroll
+  for (int i = 0; i < ftk::kR; ++i)
+    k[i] = __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane * 4, i * kWave * 4, 0));
+#pragma unroll
+  for (int i = 0; i < ftk::kR; ++i)
+    k[i] = kWave * i + lane < mine ? float_key(__builtin_bit_cast(float, k[i])) : 0u;
+  pair_topk_row(k, rounds, active, n, K, pos0, out, x, open_lists[wave]);
 }
 
 template <int H_IDX>
-__global__ __launch_bounds__(ftk::kThreads, 2) void index_topk_prefill_kernel(
+__global__ __launch_bounds__(pf::kThreads, 1) void index_topk_prefill_kernel(
     const uint16_t* __restrict__ k_idx, int64_t k_stride, const int32_t* __restrict__ block_table,
     int max_blocks, int bs, int num_blocks, QueryDesc qd, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, int n_q, int K, int32_t* __restrict__ idx,
     float* __restrict__ scratch) {
-  using ftk::kD, ftk::kKT, ftk::kLoads, ftk::kQ, ftk::kR, ftk::kRowChunks, ftk::kTileBytes;
-  constexpr int HT = H_IDX / 16, KS = kD / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kTileBytes / 2];
-  __shared__ int32_t blk[ftk::kMaxBlocks];
+  using ftk::kMaxKeys, ftk::kQ, ftk::kR;
+  __shared__ pf::Stage st;
   __shared__ BlockQueries<kQ> bq;
+  __shared__ int32_t cnt[kQ];  // candidates of each query of the block (0: none)
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int col = lane & 15, grp = lane >> 4;
-  float* row_scores = scratch + (int64_t)blockIdx.x * ftk::kSlotFloats + wave * ftk::kMaxKeys;
-  const uint32_t kt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ktile;
+  float* slot = scratch + (int64_t)blockIdx.x * ftk::kSlotFloats;
   const uint64_t row_bytes = (uint64_t)k_stride * 2;
   const int nqb = (n_q + kQ - 1) / kQ;
 
-  for (int qr = blockIdx.x; qr < nqb; qr += gridDim.x) {
-    const int q0 = (nqb - 1 - qr) * kQ;  // latest positions (usually longest rows) first
+  // Blocks in serpentine order over the grid, latest positions (usually the
+  // longest rows) first: round r gives workgroup x block t = r G + x for even
+  // r and r G + G - 1 - x for odd r, counted from the last block, so the
+  // workgroups that take a long block in one round take a short one in the
+  // next.
+  for (int r = 0;; ++r) {
+    const int t = r * (int)gridDim.x +
+                  ((r & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (t >= nqb) break;
+    const int q0 = (nqb - 1 - t) * kQ;
     const int qend = min(q0 + kQ, n_q);
-    __syncthreads();  // the previous block's bq, tiles and block entries are no longer read
+    __syncthreads();  // the previous block's bq, counts and tiles are no longer read
     bq.stage(qd, q0, qend);
     __syncthreads();
+    if (threadIdx.x < kQ) {
+      int n = bq.pos[threadIdx.x] + 1;  // 0 for no query / nothing to score
+      if (n > kMaxKeys) {
+        if (kCheckBounds) raise_error(kErrQuery);
+        n = kMaxKeys;
+      }
+      cnt[threadIdx.x] = n;
+    }
+    __syncthreads();
+    bool any = false;  // uniform: LDS data
+    for (int g = 0; g < kQ; ++g) any |= cnt[g] > K;
     const int qi = q0 + wave;
-    const int qrow = qi < qend ? qi : q0;
-    int my_n = qi < qend ? bq.pos[wave] + 1 : 0;  // candidates 0 .. my_n - 1
-    if (my_n > ftk::kMaxKeys) {
-      if (kCheckBounds && lane == 0) raise_error(kErrQuery);
-      my_n = ftk::kMaxKeys;
-    }
-    bf16x8 qa[HT][KS];
-    float wr[HT][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qa[ht][ks] = as_bf16x8(*(const u32x4*)(q_idx + ((int64_t)qrow * H_IDX + 16 * ht + col) * kD +
-                                                32 * ks + 8 * grp));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[ht][i] = w[(int64_t)qrow * H_IDX + 16 * ht + 4 * grp + i];
+
+    if (!any) {
+      // every row keeps all its candidates: 0 .. n - 1, then -1
+      if (qi < qend) {
+        const int n = cnt[wave];
+        int32_t* out = idx + (int64_t)qi * K;
+        for (int i = lane; i < K; i += kWave) out[i] = i < n ? i : -1;
+      }
+      continue;
     }
 
-    // ---- scores, one sequence of the block at a time
-    for (int lg = 0; lg < kQ; ++lg) {
-      if (!bq.lead(lg)) continue;  // uniform: LDS data
-      const int b = bq.seq[lg];
-      const int last_pos = min(bq.last_pos(b), ftk::kMaxKeys - 1);
-      const int n_tiles = last_pos / kKT + 1;
-      const int32_t* bt_row = block_table + (int64_t)b * max_blocks;
-      const int qpos = qi < qend && bq.seq[wave] == b ? min(bq.pos[wave], ftk::kMaxKeys - 1) : -1;
-      __syncthreads();  // the previous sequence's tiles and block entries are no longer read
-      for (int e = threadIdx.x; e <= last_pos / bs; e += ftk::kThreads)
-        blk[e] = checked_block(bt_row[e], num_blocks);
-      __syncthreads();
-      // Wave load i of this wave fills tile slots 64 (kLoads wave + i) + lane:
-      // slot s holds chunk (s % 16) ^ (r % 16) of tile row r = s / 16.  Rows
-      // past the last position repeat it (finite data, never stored).
-      auto load_tile = [&](int j, int buf) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-          const int bk = kLoads * wave + i;
-          const int slot = kWave * bk + lane;
-          const int r = slot / kRowChunks;
-          const int c = (slot % kRowChunks) ^ (r % kRowChunks);
-          const int pos = min(j * kKT + r, last_pos);
-          const int64_t prow = (int64_t)blk[pos / bs] * bs + pos % bs;
-          const char* src = (const char*)k_idx + (uint64_t)prow * row_bytes + 16 * c;
-          global_to_lds16(src, kt_lds + (uint32_t)(buf * kTileBytes + 16 * kWave * bk));
-        }
-      };
-      load_tile(0, 0);
-      for (int j = 0; j < n_tiles; ++j) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile j has landed
-        __syncthreads();  // all of tile j; tile j - 1's buffer is no longer read
-        if (j + 1 < n_tiles) load_tile(j + 1, (j + 1) & 1);
-        const uint16_t* kt = ktile[j & 1];
-        const int k0 = j * kKT;
-        const int n = min(kKT, max(0, qpos + 1 - k0));  // keys of this tile the query sees
-        for (int g = 0; 16 * g < n; ++g) {
-          f32x4 acc[HT];
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int r = 16 * g + col;  // B operand: key row r, dims 32 ks + 8 grp ..
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int slot = r * kRowChunks + ((4 * ks + grp) ^ (r % kRowChunks));
-            const bf16x8 kb = as_bf16x8(*(const u32x4*)(kt + 8 * slot));
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(qa[ht][ks], kb, acc[ht]);
-          }
-          float sc = 0.f;
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc += wr[ht][i] * relu(acc[ht][i]);
-          sc = wave_sum_xor_16_32(sc);
-          if (grp == 0 && r < n) row_scores[k0 + r] = sc;
-        }
+    // ---- scores of the rows with more than K candidates, into the slot
+    {
+      // the thread index passed through an opaque move: values derived from
+      // it are then computed per block rather than kept live across the
+      // whole loop (which would spill, and each reload would wait for the
+      // tile prefetch)
+      int tid = threadIdx.x;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid));
+      const int ln = tid & (kWave - 1);
+      const int my_n = cnt[wave];
+      const bool scored = my_n > K;  // wave-uniform
+      pf::QueryRegs<H_IDX> q;
+      q.load(q_idx, w, scored ? qi : q0, ln & 15, ln >> 4);
+      for (int lg = 0; lg < kQ; ++lg) {
+        if (!bq.lead(lg)) continue;  // uniform: LDS data
+        const int b = bq.seq[lg];
+        int last = -1;  // last position any scored query of sequence b sees
+        for (int g = 0; g < kQ; ++g)
+          if (bq.seq[g] == b && cnt[g] > K) last = max(last, cnt[g] - 1);
+        if (last < 0) continue;
+        const int qpos = scored && bq.seq[wave] == b ? my_n - 1 : -1;
+        pf::score_sequence<H_IDX>(st, k_idx, row_bytes, block_table + (int64_t)b * max_blocks,
+                                  bs, num_blocks, 0, last + 1, qpos, q, slot + wave * kMaxKeys,
+                                  tid);
       }
     }
+    __syncthreads();  // every wave's scores are in the slot
 
-    // ---- selection: this wave's row, read back by this wave
-    if (qi < qend) {
-      int32_t* out = idx + (int64_t)qi * K;
-      if (my_n <= K) {
-        for (int r = lane; r < K; r += kWave) out[r] = r < my_n ? r : -1;
-      } else {
-        // the row's scores, stored by this wave's lanes, read back by all of
-        // them: a workgroup-scope release / acquire orders the two (the
-        // workgroup's waves share one L1, written through)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // the row through a buffer resource: the lane offset is one vector
-        // register and each load's offset a scalar constant (128 hoisted
-        // 64-bit addresses would not fit in the registers)
-        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)row_scores, (short)0, ftk::kMaxKeys * 4, 0x00020000);
-        uint32_t k[kR];
-        const int rounds = (my_n + kWave - 1) / kWave;
-#pragma unroll
-        for (int i = 0; i < kR; ++i) {
-          const int p = kWave * i + lane;
-          k[i] = 0u;  // no candidate (float_key of a score is never 0)
-          if (i < rounds) {
-            // entries at or past my_n are stale and masked
-            const float v = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rr, lane * 4, i * kWave * 4, 0));
-            if (p < my_n) k[i] = float_key(v);
-          }
-        }
-        wave_topk_row(k, my_n, K, out);
+    // ---- selection: the pair of waves 2p, 2p + 1 takes rows 2p and 2p + 1
+#pragma unroll 1
+    for (int rr = 0; rr < 2; ++rr) {
+      const int g = (wave & ~1) + rr;
+      const int n = q0 + g < qend ? cnt[g] : 0;
+      const bool active = n > K;  // the same in both waves of the pair
+      int32_t* out = idx + (int64_t)(q0 + g) * K;
+      if (!active && q0 + g < qend) {
+        // all candidates kept; the pair shares the writes
+        for (int i = 64 * (wave & 1) + lane; i < K; i += 128) out[i] = i < n ? i : -1;
       }
+      // wave h of the pair holds positions h * half .. (half positions per
+      // wave, a multiple of 64)
+      const int half = (n + 127) / 128 * 64;
+      const int pos0 = (wave & 1) * half;
+      const int mine = max(0, min(half, n - pos0));
+      select_pair_row(slot + g * kMaxKeys + pos0, mine, active ? 1 : 0, n, K, pos0, out);
     }
   }
 }
@@ -846,7 +1012,10 @@ dsa_status_t launch_index_score_decode_gmax(const dsa_paged_cache_t* c, const ui
 
 extern "C" size_t dsa_index_topk_prefill_ws(int32_t n_q) {
   if (n_q < 1) return 0;
-  return (size_t)dsa::ftk::kMaxGrid * dsa::ftk::kSlotFloats * sizeof(float);
+  // one slot per workgroup of the persistent grid, which never exceeds the
+  // number of 16-query blocks
+  const int64_t slots = std::min<int64_t>(dsa::ftk::kMaxGrid, ((int64_t)n_q + 15) / 16);
+  return (size_t)slots * dsa::ftk::kSlotFloats * sizeof(float);
 }
 
 extern "C" dsa_status_t dsa_index_topk_prefill(const dsa_paged_cache_t* cache,
@@ -875,7 +1044,7 @@ extern "C" dsa_status_t dsa_index_topk_prefill(const dsa_paged_cache_t* cache,
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_topk_prefill_kernel<64>,
-                                                     ftk::kThreads, 0) != hipSuccess)
+                                                     pf::kThreads, 0) != hipSuccess)
       return DSA_ERR_HIP;
     grid = std::max(1, std::min(ftk::kMaxGrid, cus * std::max(1, per_cu)));
     if (dev < 64) grid_cache[dev] = grid;
@@ -886,7 +1055,7 @@ extern "C" dsa_status_t dsa_index_topk_prefill(const dsa_paged_cache_t* cache,
                                             0x7fffffff),
                      ftk::kMaxKeys};
   hipLaunchKernelGGL(index_topk_prefill_kernel<64>, dim3((unsigned)std::min(grid, nqb)),
-                     dim3(ftk::kThreads), 0, stream, cache->k_idx, cache->k_idx_row_stride,
+                     dim3(pf::kThreads), 0, stream, cache->k_idx, cache->k_idx_row_stride,
                      cache->block_table, cache->max_blocks_per_seq, cache->block_size,
                      cache->num_blocks, qd, q_idx, w, n_q, K, idx, (float*)workspace);
   return launch_status();

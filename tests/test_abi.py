@@ -145,8 +145,10 @@ def test_index_topk_validation(L):
 def test_index_topk_prefill_validation(L):
     f = L.dsa_index_topk_prefill
     ws = L.dsa_index_topk_prefill_ws(8192)
-    assert ws == 512 * 4 * 8192 * 4                          # fixed: resident slots, not n_q
-    assert L.dsa_index_topk_prefill_ws(1) == ws
+    assert ws == 256 * 16 * 8192 * 4                         # 512 KB per resident workgroup
+    assert L.dsa_index_topk_prefill_ws(1 << 20) == ws        # bounded whatever n_q
+    assert L.dsa_index_topk_prefill_ws(1) == 16 * 8192 * 4   # one 16-query block
+    assert L.dsa_index_topk_prefill_ws(33) == 3 * 16 * 8192 * 4
     assert L.dsa_index_topk_prefill_ws(0) == 0
 
     def call(c=None, q=FAKE, w=FAKE, q_seq=FAKE, q_pos=FAKE, n_q=100, H=64, K=2048, idx=FAKE,
@@ -164,7 +166,8 @@ def test_index_topk_prefill_validation(L):
     assert call(n_q=0) == 2
     assert call(K=0) == 2 and call(K=2049) == 2
     assert call(c=cache(k_idx_row_stride=100)) == 2          # stride below width
-    assert call(ws_bytes=ws - 1) == 4
+    assert call(ws_bytes=L.dsa_index_topk_prefill_ws(100) - 1) == 4
+    assert call(ws_bytes=L.dsa_index_topk_prefill_ws(100)) == 5
     assert call(H=32) == 3                                   # indexer shape (64, 128) only
     assert call(c=cache(d_idx=64, k_idx_row_stride=64)) == 3
     assert call(c=cache(k_idx_row_stride=132)) == 3          # rows of whole 16-byte chunks
