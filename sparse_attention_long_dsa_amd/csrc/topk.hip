@@ -801,11 +801,22 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
       }
     };
     uint32_t cnt[R], eoff[R];
+    // the first kKeep rounds' values stay in registers for the write pass
+    constexpr int kKeep = 8;
+    float4 kept[kKeep];
+    int kept_p0[kKeep];
 #pragma unroll
     for (int rb = 0; rb < R; rb += B) {
       float4 x[B];
       int p0[B];
       if (rb < rounds) load_batch(rb, x, p0);
+      if (rb < kKeep) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          kept[rb + b] = x[b];
+          kept_p0[rb + b] = p0[b];
+        }
+      }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         cnt[rb + b] = 0;
@@ -824,7 +835,15 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
         if (rb < rounds) {
           float4 x[B];
           int p0[B];
-          load_batch(rb, x, p0);
+          if (rb < kKeep) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              x[b] = kept[rb + b];
+              p0[b] = kept_p0[rb + b];
+            }
+          } else {
+            load_batch(rb, x, p0);
+          }
 #pragma unroll
           for (int b = 0; b < B; ++b) {
             const float xv[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
