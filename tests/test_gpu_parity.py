@@ -744,6 +744,35 @@ def test_fused_prefill_mixed_blocks_short_rows_and_reuse():
     say("   exact on both calls")
 
 
+@pytest.mark.parametrize("K,bs", [(1, 64), (37, 16), (511, 64), (2048, 16)])
+def test_fused_prefill_odd_K_and_rows_around_K(K, bs):
+    """The fused prefill selection for K values that are not multiples of the
+    wave width, rows with exactly K - 1, K and K + 1 candidates (all kept,
+    all kept, one dropped), a partial last block of queries and both block
+    sizes, against the oracle."""
+    wl = dsa_synth.latent(f"fused_k{K}", "decode", [8192, 2500], seed=63 + K % 7, topk=K,
+                          block_size=bs)
+    rng = np.random.default_rng(K)
+    near = [p for p in (K - 2, K - 1, K) if 0 <= p < 8192]
+    pos0 = np.concatenate([near, rng.integers(0, 8192, 40 - len(near)), [8191]])
+    pos1 = rng.integers(0, 2500, 12)
+    q_seq = np.concatenate([np.zeros(len(pos0), np.int32), np.ones(len(pos1), np.int32)])
+    q_pos = np.concatenate([pos0, pos1]).astype(np.int32)
+    dc = dsa_synth.device_case(wl)
+    hc = dsa_synth.host_case(wl)
+    _, q_idx, w = dsa_synth.host_query_rows(wl, 0, len(q_seq))
+    sc = oracle.index_score(hc.k_idx, hc.block_table, wl.block_size, q_idx, w, q_seq, q_pos,
+                            ld=8192)
+    idx = oracle.topk(sc, q_pos + 1, K)
+    say(f"[fused prefill] K={K}, block size {bs}, {len(q_seq)} queries")
+    cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, v=dc.v, d_v=wl.d_v)
+    got = dsa.index_topk_prefill(cache, _dev_bf16(q_idx), torch.from_numpy(w).cuda(),
+                                 torch.from_numpy(q_seq).cuda(), torch.from_numpy(q_pos).cuda(), K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), idx)
+    say("   exact")
+
+
 def test_fused_prefill_debug_build_flags_positions_past_8192():
     D = dsa.debug_lib()
     wl = dsa_synth.latent("fused_dbg", "decode", [9000], seed=62, topk=64)
