@@ -483,6 +483,55 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_latent_kernel(
   }
 }
 
+// Log-sum-exp merge of the split partials (fp16 O, fp32 lse) for up to NS
+// splits: one wave per (query, head), lane l owns value columns 8 l ..
+// 8 l + 7 (one 16-byte load per split, one 16-byte bf16 store); every load
+// of a wave is issued before the first use, so the merge of a head costs
+// one memory round trip.
+template <int NS>
+__global__ __launch_bounds__(256) void latent_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                             const float* __restrict__ part_lse,
+                                                             int n_splits, int n_qh,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse) {
+  static_assert(kDv == 8 * kWave, "a lane owns 8 value columns");
+  const int qh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  if (qh >= n_qh) return;
+  const int qi = qh / kHeads, head = qh % kHeads;
+  const int lane = threadIdx.x & (kWave - 1);
+  float l[NS];
+  u32x4 v[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < n_splits) {
+      const int64_t p = ((int64_t)qi * n_splits + s) * kHeads + head;
+      l[s] = part_lse[p];
+      v[s] = *(const u32x4*)(part_o + p * kDv + 8 * lane);
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < n_splits) m = fmaxf(m, l[s]);
+  float acc[8] = {}, wsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < n_splits) {
+      const float wgt = l[s] == -INFINITY ? 0.f : __expf(l[s] - m);
+      wsum += wgt;
+      const f16x8 x = as_f16x8(v[s]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)x[i];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *(u32x4*)(out + (int64_t)qh * kDv + 8 * lane) = o;
+  if (lse && lane == 0) lse[qh] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 }  // namespace latent
 }  // namespace
 
@@ -497,8 +546,20 @@ void launch_latent(const dsa_paged_cache_t* c, const uint16_t* q, const int32_t*
                      c->max_blocks_per_seq, c->block_size, q, idx, n_q, K, aq,
                      plan.tiles_per_split, sm_scale * kLog2e, out, lse, part_o, part_lse,
                      plan.n_splits);
-  if (plan.n_splits > 1)
-    hipLaunchKernelGGL((attn_combine_kernel<latent::kDv, uint16_t>), dim3(n_q * latent::kHeads), dim3(128), 0,
+  if (plan.n_splits <= 1) return;
+  const int n_qh = n_q * latent::kHeads;
+  const dim3 grid((unsigned)((n_qh + 3) / 4)), block(256);
+  if (plan.n_splits <= 4)
+    hipLaunchKernelGGL(latent::latent_combine_kernel<4>, grid, block, 0, stream, part_o, part_lse,
+                       plan.n_splits, n_qh, out, lse);
+  else if (plan.n_splits <= 8)
+    hipLaunchKernelGGL(latent::latent_combine_kernel<8>, grid, block, 0, stream, part_o, part_lse,
+                       plan.n_splits, n_qh, out, lse);
+  else if (plan.n_splits <= 16)
+    hipLaunchKernelGGL(latent::latent_combine_kernel<16>, grid, block, 0, stream, part_o,
+                       part_lse, plan.n_splits, n_qh, out, lse);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<latent::kDv, uint16_t>), dim3(n_qh), dim3(128), 0,
                        stream, part_o, part_lse, plan.n_splits, latent::kHeads, out, lse);
 }
 

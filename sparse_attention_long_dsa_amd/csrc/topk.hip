@@ -175,6 +175,80 @@ struct RegCount {
   }
 };
 
+// The same search run by one wave over the keys of an LDS list ent[0 .. m)
+// (K <= m <= 64 NP), with no barrier: lane l holds entries l, l + 64, ...
+// in registers (0, an empty slot, never counts), every count is a sum of
+// ballots, and the search state is wave-uniform (scalar).  Four ballots are
+// kept live at once so that their compares write four register pairs and
+// issue back to back.
+template <int NP>
+__device__ __forceinline__ Threshold wave_select_tau(const uint2* ent, uint32_t m, uint32_t K) {
+  static_assert(NP % 4 == 0, "slots in fours");
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t k[NP];
+  uint32_t a = 0xffffffffu, o = 0u;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const uint32_t e = (uint32_t)(kWave * i + lane);
+    k[i] = e < m ? ent[e].x : 0u;
+    if (k[i]) {
+      a &= k[i];
+      o |= k[i];
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    a &= __shfl_xor(a, off);
+    o |= __shfl_xor(o, off);
+  }
+  auto count_ge = [&](uint32_t c) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < NP; i += 4) {
+      const uint64_t b0 = __ballot(k[i] >= c), b1 = __ballot(k[i + 1] >= c);
+      const uint64_t b2 = __ballot(k[i + 2] >= c), b3 = __ballot(k[i + 3] >= c);
+      asm volatile("" ::"s"(b0), "s"(b1), "s"(b2), "s"(b3));
+      n += (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
+    }
+    return n;
+  };
+  uint32_t prefix = __builtin_amdgcn_readfirstlane(a);
+  uint32_t diff = prefix ^ __builtin_amdgcn_readfirstlane(o);
+  while (diff) {
+    const uint32_t bit = 1u << (31 - __clz(diff));
+    diff &= ~bit;
+    if (count_ge(prefix | bit) >= K) prefix |= bit;
+  }
+  const uint32_t gt = prefix == 0xffffffffu ? 0u : count_ge(prefix + 1u);
+  return Threshold{prefix, K - gt};
+}
+
+// Lists of at most this many entries are searched by one wave.
+constexpr uint32_t kWaveList = 64 * kWave;
+
+// Threshold of an LDS list of K <= m <= kWaveList entries whose writes a
+// barrier has already made visible: wave 0 searches, `bc` (2 words) hands
+// the result to the block.  One barrier; every thread of the block calls it.
+__device__ __forceinline__ Threshold list_tau_by_wave(const uint2* ent, uint32_t m, uint32_t K,
+                                                      uint32_t* bc) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  if (wave == 0) {
+    Threshold th;
+    if (m <= 32u * kWave)
+      th = wave_select_tau<32>(ent, m, K);
+    else if (m <= 48u * kWave)
+      th = wave_select_tau<48>(ent, m, K);
+    else
+      th = wave_select_tau<64>(ent, m, K);
+    if (threadIdx.x == 0) {
+      bc[0] = th.tau;
+      bc[1] = th.need;
+    }
+  }
+  __syncthreads();
+  return Threshold{bc[0], bc[1]};
+}
+
 template <int R>
 __device__ __forceinline__ void thread_and_or(const uint32_t (&k)[R], uint32_t& a, uint32_t& o) {
   a = 0xffffffffu;
@@ -408,6 +482,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
   __shared__ uint2 ent[kListCap];
   __shared__ uint32_t off[kMaxChunks + 1];  // list offset of each chunk, then the total
   __shared__ uint32_t sh[Block<T>::kShWords];
+  __shared__ uint32_t bc[2];
   const int row = blockIdx.x;
   const int n = row_count(n_valid, causal_base, row, ld);
   int32_t* out = idx + (int64_t)row * K;
@@ -468,11 +543,16 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
       k[i] = ok ? g[i].x : 0u;
       if (ok) ent[e] = g[i];
     }
-    uint32_t a, o;
-    thread_and_or(k, a, o);
-    const Threshold th =
-        select_tau(blk, a, o, RegCount<R>{k}, (uint32_t)K);
-    __syncthreads();
+    Threshold th;
+    if (m <= kWaveList) {
+      __syncthreads();
+      th = list_tau_by_wave(ent, m, (uint32_t)K, bc);
+    } else {
+      uint32_t a, o;
+      thread_and_or(k, a, o);
+      th = select_tau(blk, a, o, RegCount<R>{k}, (uint32_t)K);
+      __syncthreads();
+    }
     ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
     return;
   }
@@ -533,8 +613,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
 //      position lies in a group whose maximum reaches it (intra-block
 //      reduction).  Rows of fewer than 4 K groups use both m1 and m2;
 //   2. lists, in position order, the groups that reach the bound, then the
-//      scores of those groups that reach it (ordered compaction; all loads
-//      coalesced: consecutive lanes read consecutive groups);
+//      scores of those groups that reach it (ordered compaction; a thread
+//      reads whole groups, 64 bytes each, all of its loads in flight at once);
 //   3. runs the exact threshold search and ordered compaction on that list
 //      (cross-block merge).
 // A hint (the row's K-th largest key of an earlier call, kept in the
@@ -547,8 +627,7 @@ constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kFusedList = 12288;    // list entries held in LDS
 constexpr int kFusedGroups = 4096;   // candidate groups held in LDS
 constexpr int kFusedShort = 16384;   // rows up to this are selected whole
-constexpr int kMaxRounds = 16;       // 4 * kFusedGroups / kFusedThreads
-static_assert(4 * kFusedGroups / kFusedThreads == kMaxRounds, "expansion rounds");
+constexpr int kMaxSlots = 16;        // group slots per thread (the largest RG)
 
 struct GroupMaxIn {
   const float* m1;
@@ -658,7 +737,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
   constexpr int T = kFusedThreads;
   __shared__ uint2 ent[kFusedList];
   __shared__ uint32_t cg[kFusedGroups];
-  __shared__ uint32_t sc[kMaxRounds * kFusedWaves + 1];
+  __shared__ uint32_t sc[kMaxSlots * kFusedWaves + 1];
   __shared__ uint32_t sh[Block<T>::kShWords];
   const int row = blockIdx.x;
   // candidates 0 .. n - 1: the sequence length, or the query position + 1
@@ -781,78 +860,88 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 2c. the listed groups' scores that reach the bound: item e = 4 c + v
-  // is quarter v (4 positions, one 16-byte load) of listed group c.  Rounds
-  // of T items go in batches of 4 (loads of a batch in flight together); a
-  // count pass, one ordered prefix, then a write pass that loads again.
+  // ---- 2c. the listed groups' scores that reach the bound: thread t takes
+  // listed groups t, t + T, ... (16 positions each, four 16-byte loads), all
+  // of its loads in flight together; a count, one ordered prefix, then the
+  // write of the same registers.
   uint32_t m = 0;
   if (fit) {
-    constexpr int R = kMaxRounds, B = 4;
-    const int rounds = (int)((4 * m_g + T - 1) / T);  // uniform, <= 16
-    auto load_batch = [&](int rb, float4 (&x)[B], int (&p0)[B]) {
+    constexpr int R = kFusedGroups / T;  // rounds of T groups
+    const int rounds = (int)((m_g + T - 1) / T);  // uniform
+    float4 x[R][4];
+    int p0[R];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int r = rb + b;
-        const uint32_t e = (uint32_t)(r * T) + threadIdx.x;
-        const uint32_t c = min(e >> 2, m_g - 1);
-        p0[b] = r < rounds && e < 4 * m_g ? (int)cg[c] * 16 + 4 * (int)(e & 3u) : n;
-        // p0 < ld implies p0 + 3 < ld (ld is a multiple of 4)
-        x[b] = *(const float4*)(src + min(p0[b], (int)ld - 4));
+    for (int r = 0; r < R; ++r) {
+      if (r < rounds) {
+        const uint32_t c = (uint32_t)(r * T) + threadIdx.x;
+        p0[r] = c < m_g ? (int)cg[c] * 16 : n;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)  // a quarter that starts below ld ends below it (ld % 4 == 0)
+          x[r][v] = *(const float4*)(src + min(p0[r] + 4 * v, (int)ld - 4));
       }
-    };
-    uint32_t cnt[R], eoff[R];
-    // the first kKeep rounds' values stay in registers for the write pass
-    constexpr int kKeep = 8;
-    float4 kept[kKeep];
-    int kept_p0[kKeep];
+    }
+    // hit[r]: bit 4 v + q set when position p0 + 4 v + q is a candidate
+    // (below n) whose key reaches the bound.  For a bound above the key of
+    // +0 (scores above 0: the usual case) that is one signed compare of the
+    // raw bits, bits >= bound - 2^31, exact for every bit pattern: negative
+    // values, -0 and negative NaNs fall below, positive NaNs (keys above
+    // every finite one) reach it.  Otherwise the keys are formed.
+    const bool pos_bound = bound > 0x80000000u;  // uniform
+    const int bits_min = (int)(bound - 0x80000000u);
+    uint32_t hit[R], cnt[R], eoff[R];
 #pragma unroll
-    for (int rb = 0; rb < R; rb += B) {
-      float4 x[B];
-      int p0[B];
-      if (rb < rounds) load_batch(rb, x, p0);
-      if (rb < kKeep) {
+    for (int r = 0; r < R; ++r) {
+      hit[r] = 0;
+      if (r < rounds) {
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          kept[rb + b] = x[b];
-          kept_p0[rb + b] = p0[b];
+        for (int v = 0; v < 4; ++v) {
+          const float xv[4] = {x[r][v].x, x[r][v].y, x[r][v].z, x[r][v].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool h = pos_bound ? __float_as_int(xv[q]) >= bits_min : float_key(xv[q]) >= bound;
+            hit[r] |= h ? 1u << (4 * v + q) : 0u;
+          }
         }
+        const int valid = n - p0[r];  // candidates in the group (the last one may be short)
+        if (valid < 16) hit[r] &= valid > 0 ? (1u << valid) - 1u : 0u;
       }
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        cnt[rb + b] = 0;
-        if (rb < rounds) {
-          const float xv[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            cnt[rb + b] += p0[b] + q < n && float_key(xv[q]) >= bound ? 1u : 0u;
-        }
-      }
+      cnt[r] = (uint32_t)__popc(hit[r]);
     }
     m = slot_major_offsets(cnt, rounds, eoff, sc);
     if (m <= (uint32_t)kFusedList) {
+      // the hits of each group, lowest position first; a hit's score is
+      // picked out of the group's 16 registers by the bits of its index
 #pragma unroll
-      for (int rb = 0; rb < R; rb += B) {
-        if (rb < rounds) {
-          float4 x[B];
-          int p0[B];
-          if (rb < kKeep) {
+      for (int r = 0; r < R; ++r) {
+        if (r < rounds) {
+          const float f[16] = {x[r][0].x, x[r][0].y, x[r][0].z, x[r][0].w,
+                               x[r][1].x, x[r][1].y, x[r][1].z, x[r][1].w,
+                               x[r][2].x, x[r][2].y, x[r][2].z, x[r][2].w,
+                               x[r][3].x, x[r][3].y, x[r][3].z, x[r][3].w};
+          uint32_t at = eoff[r], h = hit[r];
+          while (h) {
+            const int q = __builtin_ctz(h);
+            h &= h - 1u;
+            // (selects of values, not of array elements: a conditional of two
+            // lvalues would select an address and keep f in scratch memory)
+            float g[8], k4[4], k2[2];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-              x[b] = kept[rb + b];
-              p0[b] = kept_p0[rb + b];
+            for (int i = 0; i < 8; ++i) {
+              const float lo = f[i], hi = f[8 + i];
+              g[i] = (q & 8) ? hi : lo;
             }
-          } else {
-            load_batch(rb, x, p0);
-          }
 #pragma unroll
-          for (int b = 0; b < B; ++b) {
-            const float xv[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
-            uint32_t at = eoff[rb + b];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t k = float_key(xv[q]);
-              if (p0[b] + q < n && k >= bound) ent[at++] = make_uint2(k, (uint32_t)(p0[b] + q));
+            for (int i = 0; i < 4; ++i) {
+              const float lo = g[i], hi = g[4 + i];
+              k4[i] = (q & 4) ? hi : lo;
             }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const float lo = k4[i], hi = k4[2 + i];
+              k2[i] = (q & 2) ? hi : lo;
+            }
+            const float lo = k2[0], hi = k2[1];
+            ent[at++] = make_uint2(float_key((q & 1) ? hi : lo), (uint32_t)(p0[r] + q));
           }
         }
       }
@@ -865,8 +954,14 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 3. exact search and ordered compaction over the list (m >= K);
-  // thread t holds entries t, t + T, ...
+  // ---- 3. exact search and ordered compaction over the list (m >= K): by
+  // one wave for short lists, else thread t holds entries t, t + T, ...
+  if (m <= kWaveList) {
+    const Threshold th = list_tau_by_wave(ent, m, (uint32_t)K, sc);
+    ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
+    if (threadIdx.x == 0) gm.tau[row] = th.tau;
+    return;
+  }
   constexpr int RL = kFusedList / T;
   const int rl = (int)((m + T - 1) / T);  // uniform
   uint32_t kl[RL];

@@ -544,6 +544,7 @@ def _fused_case(wl, hc, what):
     dc.k_idx.copy_(torch.from_numpy(hc.k_idx.view(np.int16)).view(torch.bfloat16)
                    .reshape(dc.k_idx.shape))
     dc.q_idx.copy_(torch.from_numpy(hc.q_idx.view(np.int16)).view(torch.bfloat16))
+    dc.w.copy_(torch.from_numpy(hc.w))
     cache = dsa.Cache(dc.kv, dc.k_idx, dc.block_table, dc.seq_lens, d_v=wl.d_v)
     ld = max(wl.seq_lens)
     fused = dsa.DecodeStep(cache, wl.n_q, wl.H, wl.H_idx, wl.topk, ld, wl.d_v)
@@ -588,6 +589,29 @@ def test_fused_topk_score_patterns():
     hc.k_idx[r[-1:]] = 0x4040  # 3.0
     hc.q_idx[4] = one
     _fused_case(wl, hc, "patterns")
+
+
+@pytest.mark.parametrize("K,n_a,n_b", [(1000, 900, 400), (2048, 2000, 1000), (2048, 2000, 1500),
+                                       (2048, 2000, 2500)])
+def test_fused_topk_ties_in_the_candidate_list(K, n_a, n_b):
+    """Ties at the K-th score inside the candidate list.  In a 65000-position
+    row, n_a positions share the highest score and n_b the second highest
+    (every 13th position, so each is the maximum of its 16-position group),
+    all others score far lower: the bound is the second score, the list holds
+    exactly the n_a + n_b positions (1300, 3000, 3500: searched by one wave;
+    4500: by the whole workgroup), and the kept ones are the n_a and the
+    lowest K - n_a of the n_b."""
+    L = 65000
+    wl = dsa_synth.latent("fused_ties", "decode", [L, 30000], seed=75, topk=K, H_idx=64)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    r = _logical_rows(wl, hc.block_table, 0, L)
+    hc.q_idx[0] = 0x3F80  # q = 1: a score is relu(sum of the key row) * sum(w), w >= 1
+    hc.k_idx[r[13 * np.arange(n_a)]] = 0x4040           # 3.0: sum 384
+    hc.k_idx[r[30000 + 13 * np.arange(n_b)]] = 0x4000   # 2.0: sum 256 (random rows: |sum| < 150)
+    f = _fused_case(wl, hc, f"ties at the K-th score: K={K}, {n_a} + {n_b} listed")
+    kept = f.idx[0].cpu().numpy()
+    np.testing.assert_array_equal(
+        kept, np.concatenate([13 * np.arange(n_a), 30000 + 13 * np.arange(K - n_a)]))
 
 
 def test_fused_topk_small_K():
