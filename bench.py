@@ -54,7 +54,7 @@ KERNEL_SOURCES = {
     "index_score_decode": ["index_score.hip", "common.h"],
     "topk_fused": ["topk.hip", "common.h"],
     "sparse_attn_latent": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
-    "attn_combine": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
+    "latent_combine": ["sparse_attn_latent.hip", "attn_common.h", "common.h"],
     "topk": ["topk.hip", "common.h"],
     "moe_decode": ["moe.hip", "common.h"],
     "moe_prefill": ["moe.hip", "common.h"],

@@ -499,30 +499,27 @@ __global__ __launch_bounds__(256) void latent_combine_kernel(const uint16_t* __r
   if (qh >= n_qh) return;
   const int qi = qh / kHeads, head = qh % kHeads;
   const int lane = threadIdx.x & (kWave - 1);
+  // unconditional loads (slots past n_splits repeat the last split and get
+  // weight 0): no branch between the loads
   float l[NS];
   u32x4 v[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s < n_splits) {
-      const int64_t p = ((int64_t)qi * n_splits + s) * kHeads + head;
-      l[s] = part_lse[p];
-      v[s] = *(const u32x4*)(part_o + p * kDv + 8 * lane);
-    }
+    const int64_t p = ((int64_t)qi * n_splits + min(s, n_splits - 1)) * kHeads + head;
+    l[s] = part_lse[p];
+    v[s] = *(const u32x4*)(part_o + p * kDv + 8 * lane);
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < n_splits) m = fmaxf(m, l[s]);
+  for (int s = 0; s < NS; ++s) m = fmaxf(m, l[s]);
   float acc[8] = {}, wsum = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s < n_splits) {
-      const float wgt = l[s] == -INFINITY ? 0.f : __expf(l[s] - m);
-      wsum += wgt;
-      const f16x8 x = as_f16x8(v[s]);
+    const float wgt = s >= n_splits || l[s] == -INFINITY ? 0.f : __expf(l[s] - m);
+    wsum += wgt;
+    const f16x8 x = as_f16x8(v[s]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)x[i];
-    }
+    for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)x[i];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   u32x4 o;
