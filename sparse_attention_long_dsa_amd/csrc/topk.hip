@@ -11,11 +11,14 @@
 // the K-th largest score is found by a bitwise search: starting from the
 // bits every key shares, each bit where keys differ is tried from the top,
 // and kept when at least K keys are >= the candidate.  The count is made
-// with wave64 ballot bitmasks and popcounts (no histogram, no atomics), so
-// scores that crowd into a narrow range cost nothing extra.  Every key above
-// tau is kept, and of the keys equal to tau the `need` lowest positions;
-// an ordered compaction (per-thread counts and one block prefix scan) writes
-// the kept positions in ascending order.  Nothing is ever sorted.
+// with wave64 ballot bitmasks and popcounts, so scores that crowd into a
+// narrow range cost nothing extra.  The short candidate lists of the last
+// step are searched by radix passes instead (8 bits a pass, a 256-bin LDS
+// histogram per wave built with one atomic add per key): far fewer
+// barriers than one per bit.  Every key above tau is kept, and of the keys
+// equal to tau the `need` lowest positions; an ordered compaction
+// (per-thread counts and one block prefix scan) writes the kept positions
+// in ascending order.  Nothing is ever sorted.
 //
 // Two paths, chosen by the row capacity `ld`:
 //   ld <= 16384: one workgroup per row holds the row (prefill rows);
@@ -175,78 +178,74 @@ struct RegCount {
   }
 };
 
-// The same search run by one wave over the keys of an LDS list ent[0 .. m)
-// (K <= m <= 64 NP), with no barrier: lane l holds entries l, l + 64, ...
-// in registers (0, an empty slot, never counts), every count is a sum of
-// ballots, and the search state is wave-uniform (scalar).  Four ballots are
-// kept live at once so that their compares write four register pairs and
-// issue back to back.
-template <int NP>
-__device__ __forceinline__ Threshold wave_select_tau(const uint2* ent, uint32_t m, uint32_t K) {
-  static_assert(NP % 4 == 0, "slots in fours");
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t k[NP];
+// The same threshold by radix passes: from the highest bit where the keys
+// differ, 8 bits at a time, every thread adds its live keys (those equal to
+// the prefix on every bit decided so far) to its wave's 256-bin histogram
+// of the next digit in LDS (one atomic add per key), and a suffix sum over
+// the bins picks the digit that holds the K-th largest; the keys of higher
+// digits are counted as above every later candidate.  Thread t holds the
+// keys k[i] (i < rl, uniform; 0 marks an empty slot, never counted).
+// `hist` holds 256 words per wave, `bc` 4 words; four barriers a pass.
+template <int T, int R>
+__device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], int rl, uint32_t K,
+                                      uint32_t* hist, uint32_t* bc) {
+  constexpr int W = T / kWave;
+  static_assert(T >= 256, "one thread per bin");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   uint32_t a = 0xffffffffu, o = 0u;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const uint32_t e = (uint32_t)(kWave * i + lane);
-    k[i] = e < m ? ent[e].x : 0u;
-    if (k[i]) {
+  for (int i = 0; i < R; ++i)
+    if (i < rl && k[i]) {
       a &= k[i];
       o |= k[i];
     }
-  }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    a &= __shfl_xor(a, off);
-    o |= __shfl_xor(o, off);
-  }
-  auto count_ge = [&](uint32_t c) {
-    uint32_t n = 0;
-#pragma unroll
-    for (int i = 0; i < NP; i += 4) {
-      const uint64_t b0 = __ballot(k[i] >= c), b1 = __ballot(k[i + 1] >= c);
-      const uint64_t b2 = __ballot(k[i + 2] >= c), b3 = __ballot(k[i + 3] >= c);
-      asm volatile("" ::"s"(b0), "s"(b1), "s"(b2), "s"(b3));
-      n += (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
-    }
-    return n;
-  };
-  uint32_t prefix = __builtin_amdgcn_readfirstlane(a);
-  uint32_t diff = prefix ^ __builtin_amdgcn_readfirstlane(o);
+  blk.and_or(a, o);
+  uint32_t prefix = a, diff = a ^ o, above = 0;
   while (diff) {
-    const uint32_t bit = 1u << (31 - __clz(diff));
-    diff &= ~bit;
-    if (count_ge(prefix | bit) >= K) prefix |= bit;
-  }
-  const uint32_t gt = prefix == 0xffffffffu ? 0u : count_ge(prefix + 1u);
-  return Threshold{prefix, K - gt};
-}
-
-// Lists of at most this many entries are searched by one wave.
-constexpr uint32_t kWaveList = 64 * kWave;
-
-// Threshold of an LDS list of K <= m <= kWaveList entries whose writes a
-// barrier has already made visible: wave 0 searches, `bc` (2 words) hands
-// the result to the block.  One barrier; every thread of the block calls it.
-__device__ __forceinline__ Threshold list_tau_by_wave(const uint2* ent, uint32_t m, uint32_t K,
-                                                      uint32_t* bc) {
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-  if (wave == 0) {
-    Threshold th;
-    if (m <= 32u * kWave)
-      th = wave_select_tau<32>(ent, m, K);
-    else if (m <= 48u * kWave)
-      th = wave_select_tau<48>(ent, m, K);
-    else
-      th = wave_select_tau<64>(ent, m, K);
-    if (threadIdx.x == 0) {
-      bc[0] = th.tau;
-      bc[1] = th.need;
+    const int hi = 31 - __clz(diff), lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (hi == 31 ? 0xffffffffu : (2u << hi) - 1u) & ~((1u << lo) - 1u);
+    const uint32_t M = hi == 31 ? 0u : ~((2u << hi) - 1u);  // the bits decided
+    const uint32_t pm = prefix & M;
+    for (int j = threadIdx.x; j < 256 * W; j += T) hist[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (i < rl && k[i] != 0u && (k[i] & M) == pm)
+        atomicAdd(&hist[256 * wave + ((k[i] & dmask) >> lo)], 1u);
+    __syncthreads();
+    // thread b < 256: the keys of digit b, then the sum over digits >= b
+    // (a scan from the top within each wave, then across the four waves)
+    uint32_t tot = 0, suf = 0;
+    if (threadIdx.x < 256) {
+      const int b = threadIdx.x;
+#pragma unroll
+      for (int w = 0; w < W; ++w) tot += hist[256 * w + b];
+      suf = tot;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_down(suf, d);
+        if (lane + d < kWave) suf += y;
+      }
+      if (lane == 0) bc[wave] = suf;  // wave total (bins 64 wave .. 64 wave + 63)
     }
+    __syncthreads();
+    const uint32_t need = K - above;
+    if (threadIdx.x < 256) {
+      for (int w = wave + 1; w < 4; ++w) suf += bc[w];
+      // the digit: the largest b whose suffix reaches need
+      if (suf >= need && suf - tot < need) {
+        bc[4] = (uint32_t)threadIdx.x;
+        bc[5] = suf - tot;  // keys of higher digits
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = bc[4];
+    above += bc[5];
+    prefix = (prefix & ~dmask) | (digit << lo);
+    diff &= ~dmask;
+    __syncthreads();  // bc and hist are rewritten by the next pass
   }
-  __syncthreads();
-  return Threshold{bc[0], bc[1]};
+  return Threshold{prefix, K - above};
 }
 
 template <int R>
@@ -482,7 +481,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
   __shared__ uint2 ent[kListCap];
   __shared__ uint32_t off[kMaxChunks + 1];  // list offset of each chunk, then the total
   __shared__ uint32_t sh[Block<T>::kShWords];
-  __shared__ uint32_t bc[2];
+  __shared__ uint32_t bc[8];
   const int row = blockIdx.x;
   const int n = row_count(n_valid, causal_base, row, ld);
   int32_t* out = idx + (int64_t)row * K;
@@ -543,16 +542,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
       k[i] = ok ? g[i].x : 0u;
       if (ok) ent[e] = g[i];
     }
-    Threshold th;
-    if (m <= kWaveList) {
-      __syncthreads();
-      th = list_tau_by_wave(ent, m, (uint32_t)K, bc);
-    } else {
-      uint32_t a, o;
-      thread_and_or(k, a, o);
-      th = select_tau(blk, a, o, RegCount<R>{k}, (uint32_t)K);
-      __syncthreads();
-    }
+    // the chunk offsets are no longer needed: their words hold the histograms
+    __syncthreads();
+    const Threshold th = radix_select_tau(blk, k, (int)rr, (uint32_t)K, off, bc);
     ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
     return;
   }
@@ -615,8 +607,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
 //   2. lists, in position order, the groups that reach the bound, then the
 //      scores of those groups that reach it (ordered compaction; a thread
 //      reads whole groups, 64 bytes each, all of its loads in flight at once);
-//   3. runs the exact threshold search and ordered compaction on that list
-//      (cross-block merge).
+//   3. runs the exact threshold search (radix passes) and ordered
+//      compaction on that list (cross-block merge).
 // A hint (the row's K-th largest key of an earlier call, kept in the
 // workspace) replaces step 1's search when at least K and at most 2 K of the
 // group maxima reach it.  When a list would overflow LDS the row is selected
@@ -954,14 +946,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 3. exact search and ordered compaction over the list (m >= K): by
-  // one wave for short lists, else thread t holds entries t, t + T, ...
-  if (m <= kWaveList) {
-    const Threshold th = list_tau_by_wave(ent, m, (uint32_t)K, sc);
-    ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
-    if (threadIdx.x == 0) gm.tau[row] = th.tau;
-    return;
-  }
+  // ---- 3. exact search (radix passes) and ordered compaction over the list
   constexpr int RL = kFusedList / T;
   const int rl = (int)((m + T - 1) / T);  // uniform
   uint32_t kl[RL];
@@ -970,16 +955,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
     const uint32_t e = (uint32_t)(i * T) + threadIdx.x;
     kl[i] = i < rl && e < m ? ent[e].x : 0u;
   }
-  uint32_t a, o;
-  thread_and_or(kl, a, o);
-  auto list_ge = [&](uint32_t c) {
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < RL; ++i)
-      if (i < rl) cnt += (uint32_t)__popcll(__ballot(kl[i] >= c));
-    return cnt;
-  };
-  const Threshold th = select_tau(blk, a, o, list_ge, (uint32_t)K);
+  const Threshold th = radix_select_tau(blk, kl, rl, (uint32_t)K, cg, sc);
   ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
   if (threadIdx.x == 0) gm.tau[row] = th.tau;
 }
