@@ -68,6 +68,52 @@ __device__ __forceinline__ int row_count(const int32_t* n_valid, int causal_base
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
+// Wave-wide scans and reductions on the DPP row shifts and row broadcasts:
+// VALU operations, where a shuffle is an LDS round trip.  A lane whose DPP
+// source does not exist (or whose row is masked off) reads `old`, the
+// operation's identity.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes: within each row of 16 by shifts
+// of 1, 2, 4, 8, then row 0's total into row 1 and row 2's into row 3, then
+// lane 31's running total into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+  v += dpp<kRowShr1>(0u, v);
+  v += dpp<kRowShr2>(0u, v);
+  v += dpp<kRowShr4>(0u, v);
+  v += dpp<kRowShr8>(0u, v);
+  v += dpp<kRowBcast15, 0xa>(0u, v);
+  v += dpp<kRowBcast31, 0xc>(0u, v);
+  return v;
+}
+// Sum, AND and OR over the wave (the same steps; lane 63 holds the result).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_add(v), kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= dpp<kRowShr1>(~0u, v);
+  v &= dpp<kRowShr2>(~0u, v);
+  v &= dpp<kRowShr4>(~0u, v);
+  v &= dpp<kRowShr8>(~0u, v);
+  v &= dpp<kRowBcast15, 0xa>(~0u, v);
+  v &= dpp<kRowBcast31, 0xc>(~0u, v);
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp<kRowShr1>(0u, v);
+  v |= dpp<kRowShr2>(0u, v);
+  v |= dpp<kRowShr4>(0u, v);
+  v |= dpp<kRowShr8>(0u, v);
+  v |= dpp<kRowBcast15, 0xa>(0u, v);
+  v |= dpp<kRowBcast31, 0xc>(0u, v);
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
 // Block-wide reductions over T threads through a double-buffered LDS area
 // (`sh` holds kShWords words): one barrier per call, and two consecutive
 // calls never touch the same words.
@@ -93,18 +139,11 @@ struct Block {
     for (int w = 0; w < kW; ++w) s += b[w];
     return s;
   }
-  __device__ uint32_t sum(uint32_t v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off);
-    return sum_waves(v);
-  }
+  __device__ uint32_t sum(uint32_t v) { return sum_waves(wave_sum(v)); }
   // AND and OR of one value per thread.
   __device__ void and_or(uint32_t& a, uint32_t& o) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      a &= __shfl_xor(a, off);
-      o |= __shfl_xor(o, off);
-    }
+    a = wave_and(a);
+    o = wave_or(o);
     uint32_t* b = buf();
     if ((threadIdx.x & (kWave - 1)) == 0) {
       b[threadIdx.x / kWave] = a;
@@ -122,12 +161,7 @@ struct Block {
   // Exclusive prefix sum in thread order, and the block total.
   __device__ uint32_t prefix_excl(uint32_t v, uint32_t* total) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    uint32_t incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t x = __shfl_up(incl, off);
-      if (lane >= off) incl += x;
-    }
+    const uint32_t incl = wave_incl_add(v);
     uint32_t* b = buf();
     if (lane == kWave - 1) b[wave] = incl;
     __syncthreads();
@@ -213,28 +247,24 @@ __device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], int
       if (i < rl && k[i] != 0u && (k[i] & M) == pm)
         atomicAdd(&hist[256 * wave + ((k[i] & dmask) >> lo)], 1u);
     __syncthreads();
-    // thread b < 256: the keys of digit b, then the sum over digits >= b
-    // (a scan from the top within each wave, then across the four waves)
+    // thread t < 256 takes digit 255 - t: its keys, then (a prefix over the
+    // threads) the keys of digits >= 255 - t, within the wave and then
+    // across the four waves
     uint32_t tot = 0, suf = 0;
     if (threadIdx.x < 256) {
-      const int b = threadIdx.x;
+      const int b = 255 - (int)threadIdx.x;
 #pragma unroll
       for (int w = 0; w < W; ++w) tot += hist[256 * w + b];
-      suf = tot;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t y = __shfl_down(suf, d);
-        if (lane + d < kWave) suf += y;
-      }
-      if (lane == 0) bc[wave] = suf;  // wave total (bins 64 wave .. 64 wave + 63)
+      suf = wave_incl_add(tot);
+      if (lane == kWave - 1) bc[wave] = suf;  // wave total (digits 255 - 64 wave down)
     }
     __syncthreads();
     const uint32_t need = K - above;
     if (threadIdx.x < 256) {
-      for (int w = wave + 1; w < 4; ++w) suf += bc[w];
-      // the digit: the largest b whose suffix reaches need
+      for (int w = 0; w < wave; ++w) suf += bc[w];
+      // the digit: the largest whose keys and those above reach need
       if (suf >= need && suf - tot < need) {
-        bc[4] = (uint32_t)threadIdx.x;
+        bc[4] = 255u - threadIdx.x;
         bc[5] = suf - tot;  // keys of higher digits
       }
     }
@@ -566,9 +596,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
   auto wave_ge = [&](uint32_t c) {
     uint32_t n_ge = 0;
     for (uint32_t e = threadIdx.x; e < mm; e += T) n_ge += entry(e).x >= c ? 1u : 0u;
-#pragma unroll
-    for (int off_ = 1; off_ < kWave; off_ <<= 1) n_ge += __shfl_xor(n_ge, off_);
-    return n_ge;
+    return wave_sum(n_ge);
   };
   const Threshold th = select_tau(blk, a, o, wave_ge, (uint32_t)K);
   // ordered compaction in rounds of T entries (the list may exceed 65535)
@@ -583,8 +611,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
     const uint32_t packed = (uint32_t)__popcll(mgt) | ((uint32_t)__popcll(meq) << 16);
     uint32_t tot;
     const uint32_t before = blk.prefix_excl(lane == 0 ? packed : 0u, &tot);
-    const uint32_t wave_gt = (__shfl(before, 0) & 0xffffu) + (uint32_t)__popcll(mgt & lanemask_lt(lane));
-    const uint32_t wave_eq = (__shfl(before, 0) >> 16) + (uint32_t)__popcll(meq & lanemask_lt(lane));
+    const uint32_t b0 = __builtin_amdgcn_readlane(before, 0);
+    const uint32_t wave_gt = (b0 & 0xffffu) + (uint32_t)__popcll(mgt & lanemask_lt(lane));
+    const uint32_t wave_eq = (b0 >> 16) + (uint32_t)__popcll(meq & lanemask_lt(lane));
     const uint32_t eq_rank = eq_base + wave_eq;
     if (gt || (eq && eq_rank < th.need)) out[gt_base + wave_gt + min(eq_rank, th.need)] = (int32_t)v.y;
     gt_base += tot & 0xffffu;
@@ -646,9 +675,7 @@ __device__ uint32_t select_row_global(Block<T>& blk, const float* __restrict__ s
   auto wave_ge = [&](uint32_t c) {
     uint32_t n_ge = 0;
     for (uint32_t e = threadIdx.x; e < n; e += T) n_ge += float_key(src[e]) >= c ? 1u : 0u;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) n_ge += __shfl_xor(n_ge, off);
-    return n_ge;
+    return wave_sum(n_ge);
   };
   const Threshold th = select_tau(blk, a, o, wave_ge, K);
   const int lane = threadIdx.x & (kWave - 1);
@@ -662,8 +689,9 @@ __device__ uint32_t select_row_global(Block<T>& blk, const float* __restrict__ s
     const uint32_t packed = (uint32_t)__popcll(mgt) | ((uint32_t)__popcll(meq) << 16);
     uint32_t tot;
     const uint32_t before = blk.prefix_excl(lane == 0 ? packed : 0u, &tot);
-    const uint32_t wave_gt = (__shfl(before, 0) & 0xffffu) + (uint32_t)__popcll(mgt & lanemask_lt(lane));
-    const uint32_t wave_eq = (__shfl(before, 0) >> 16) + (uint32_t)__popcll(meq & lanemask_lt(lane));
+    const uint32_t b0 = __builtin_amdgcn_readlane(before, 0);
+    const uint32_t wave_gt = (b0 & 0xffffu) + (uint32_t)__popcll(mgt & lanemask_lt(lane));
+    const uint32_t wave_eq = (b0 >> 16) + (uint32_t)__popcll(meq & lanemask_lt(lane));
     const uint32_t eq_rank = eq_base + wave_eq;
     if (gt || (eq && eq_rank < th.need)) out[gt_base + wave_gt + min(eq_rank, th.need)] = (int32_t)e;
     gt_base += tot & 0xffffu;
@@ -685,14 +713,8 @@ __device__ uint32_t slot_major_offsets(const uint32_t (&c)[R], int n_slots, uint
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (i < n_slots) {
-    uint32_t x = c[i];
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const uint32_t y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
-    incl[i] = x;
-    if (lane == kWave - 1) sc[i * kFusedWaves + wave] = x;
+      incl[i] = wave_incl_add(c[i]);
+      if (lane == kWave - 1) sc[i * kFusedWaves + wave] = incl[i];
     }
   }
   __syncthreads();
@@ -701,12 +723,7 @@ __device__ uint32_t slot_major_offsets(const uint32_t (&c)[R], int n_slots, uint
     const int per = (n + kWave - 1) / kWave;
     uint32_t run = 0;
     for (int e = lane * per; e < min(n, lane * per + per); ++e) run += sc[e];
-    uint32_t x = run;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const uint32_t y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
+    const uint32_t x = wave_incl_add(run);
     uint32_t acc = x - run;
     for (int e = lane * per; e < min(n, lane * per + per); ++e) {
       const uint32_t v = sc[e];
