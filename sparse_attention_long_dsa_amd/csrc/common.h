@@ -171,6 +171,52 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 // Order-preserving map of fp32 onto uint32: larger float -> larger key.
 // -0.0 is folded onto +0.0 so the two compare equal.
+// Wave-wide scans and reductions on the DPP row shifts and row broadcasts:
+// VALU operations, where a shuffle is an LDS round trip.  A lane whose DPP
+// source does not exist (or whose row is masked off) reads `old`, the
+// operation's identity.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes: within each row of 16 by shifts
+// of 1, 2, 4, 8, then row 0's total into row 1 and row 2's into row 3, then
+// lane 31's running total into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+  v += dpp<kRowShr1>(0u, v);
+  v += dpp<kRowShr2>(0u, v);
+  v += dpp<kRowShr4>(0u, v);
+  v += dpp<kRowShr8>(0u, v);
+  v += dpp<kRowBcast15, 0xa>(0u, v);
+  v += dpp<kRowBcast31, 0xc>(0u, v);
+  return v;
+}
+// Sum, AND and OR over the wave (the same steps; lane 63 holds the result).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_add(v), kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= dpp<kRowShr1>(~0u, v);
+  v &= dpp<kRowShr2>(~0u, v);
+  v &= dpp<kRowShr4>(~0u, v);
+  v &= dpp<kRowShr8>(~0u, v);
+  v &= dpp<kRowBcast15, 0xa>(~0u, v);
+  v &= dpp<kRowBcast31, 0xc>(~0u, v);
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp<kRowShr1>(0u, v);
+  v |= dpp<kRowShr2>(0u, v);
+  v |= dpp<kRowShr4>(0u, v);
+  v |= dpp<kRowShr8>(0u, v);
+  v |= dpp<kRowBcast15, 0xa>(0u, v);
+  v |= dpp<kRowBcast31, 0xc>(0u, v);
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0;

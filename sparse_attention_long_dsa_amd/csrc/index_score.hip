@@ -701,13 +701,8 @@ __device__ __forceinline__ void pair_topk_row(const uint32_t (&k)[ftk::kR], int 
       a &= k[i];
       o |= k[i];
     }
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    a &= __shfl_xor(a, d);
-    o |= __shfl_xor(o, d);
-  }
-  a = uni(a);
-  o = uni(o);
+  a = wave_and(a);  // wave-uniform (read from lane 63)
+  o = wave_or(o);
   if (lane == 0) {
     x.a[wave] = a;
     x.o[wave] = o;
