@@ -172,18 +172,22 @@ struct RegCount {
 // of the next digit in LDS (one atomic add per key), and a suffix sum over
 // the bins picks the digit that holds the K-th largest; the keys of higher
 // digits are counted as above every later candidate.  Thread t holds the
-// keys k[i] (i < rl, uniform; 0 marks an empty slot, never counted).
-// `hist` holds 256 words per wave, `bc` 4 words; four barriers a pass.
-template <int T, int R>
-__device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], int rl, uint32_t K,
-                                      uint32_t* hist, uint32_t* bc) {
+// keys k[i] of the slots where valid(i) (uniform; 0 marks an empty slot,
+// never counted).  With stop > 0 the search ends as soon as at most `stop`
+// keys reach the value decided so far (lower bits as in the prefix): that
+// value, which at least K keys reach, is returned as tau (need is then
+// meaningless).  `hist` holds 256 words per wave, `bc` 7 words; four
+// barriers a pass.
+template <int T, int R, class Valid>
+__device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], Valid valid,
+                                      uint32_t K, uint32_t stop, uint32_t* hist, uint32_t* bc) {
   constexpr int W = T / kWave;
   static_assert(T >= 256, "one thread per bin");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   uint32_t a = 0xffffffffu, o = 0u;
 #pragma unroll
   for (int i = 0; i < R; ++i)
-    if (i < rl && k[i]) {
+    if (valid(i) && k[i]) {
       a &= k[i];
       o |= k[i];
     }
@@ -198,7 +202,7 @@ __device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], int
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < R; ++i)
-      if (i < rl && k[i] != 0u && (k[i] & M) == pm)
+      if (valid(i) && k[i] != 0u && (k[i] & M) == pm)
         atomicAdd(&hist[256 * wave + ((k[i] & dmask) >> lo)], 1u);
     __syncthreads();
     // thread t < 256 takes digit 255 - t: its keys, then (a prefix over the
@@ -220,14 +224,16 @@ __device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], int
       if (suf >= need && suf - tot < need) {
         bc[4] = 255u - threadIdx.x;
         bc[5] = suf - tot;  // keys of higher digits
+        bc[6] = suf;        // keys of this digit and higher ones
       }
     }
     __syncthreads();
-    const uint32_t digit = bc[4];
+    const uint32_t digit = bc[4], reach = above + bc[6];  // keys >= the new prefix
     above += bc[5];
     prefix = (prefix & ~dmask) | (digit << lo);
     diff &= ~dmask;
     __syncthreads();  // bc and hist are rewritten by the next pass
+    if (stop && reach <= stop) break;
   }
   return Threshold{prefix, K - above};
 }
@@ -528,7 +534,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(
     }
     // the chunk offsets are no longer needed: their words hold the histograms
     __syncthreads();
-    const Threshold th = radix_select_tau(blk, k, (int)rr, (uint32_t)K, off, bc);
+    const Threshold th =
+        radix_select_tau(blk, k, [&](int i) { return i < (int)rr; }, (uint32_t)K, 0u, off, bc);
     ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
     return;
   }
@@ -781,33 +788,17 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
     }
   }
   if (!have) {
-    // bitwise search for the K-th largest key, stopped once at most 5 K / 4
-    // keys reach the prefix (any value that K keys reach is a valid bound)
-    uint32_t a = 0xffffffffu, o = 0u;
+    // radix passes towards the K-th largest key, stopped once at most 5 K / 4
+    // keys reach the value decided (any value that K keys reach is a valid
+    // bound)
+    uint32_t kk[2 * RG];
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
-      if (k1[i]) {
-        a &= k1[i];
-        o |= k1[i];
-      }
-      if (k2[i]) {
-        a &= k2[i];
-        o |= k2[i];
-      }
+      kk[i] = k1[i];
+      kk[RG + i] = k2[i];
     }
-    blk.and_or(a, o);
-    uint32_t prefix = a, diff = a ^ o;
-    const uint32_t stop = (uint32_t)K + (uint32_t)K / 4;
-    while (diff) {
-      const uint32_t bit = 1u << (31 - __clz(diff));
-      diff &= ~bit;
-      const uint32_t c = blk.sum_waves(count_ge(prefix | bit));
-      if (c >= (uint32_t)K) {
-        prefix |= bit;
-        if (c <= stop) break;
-      }
-    }
-    bound = prefix;
+    bound = radix_select_tau(blk, kk, [&](int i) { return (i % RG) < n_slots; }, (uint32_t)K,
+                             (uint32_t)K + (uint32_t)K / 4, cg, sc).tau;
   }
 
   // ---- 2a. candidate groups (maximum >= bound), in position order
@@ -926,7 +917,8 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
     const uint32_t e = (uint32_t)(i * T) + threadIdx.x;
     kl[i] = i < rl && e < m ? ent[e].x : 0u;
   }
-  const Threshold th = radix_select_tau(blk, kl, rl, (uint32_t)K, cg, sc);
+  const Threshold th =
+      radix_select_tau(blk, kl, [&](int i) { return i < rl; }, (uint32_t)K, 0u, cg, sc);
   ordered_compact(blk, m, th, [&](uint32_t e) { return ent[e]; }, out);
   if (threadIdx.x == 0) gm.tau[row] = th.tau;
 }
