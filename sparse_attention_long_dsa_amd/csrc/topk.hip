@@ -178,9 +178,15 @@ struct RegCount {
 // value, which at least K keys reach, is returned as tau (need is then
 // meaningless).  `hist` holds 256 words per wave, `bc` 7 words; four
 // barriers a pass.
-template <int T, int R, class Valid>
+// on_pass(prefix) runs (in every thread) after each pass with the value
+// decided so far.
+struct NoPass {
+  __device__ void operator()(uint32_t) const {}
+};
+template <int T, int R, class Valid, class OnPass = NoPass>
 __device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], Valid valid,
-                                      uint32_t K, uint32_t stop, uint32_t* hist, uint32_t* bc) {
+                                      uint32_t K, uint32_t stop, uint32_t* hist, uint32_t* bc,
+                                      OnPass on_pass = OnPass()) {
   constexpr int W = T / kWave;
   static_assert(T >= 256, "one thread per bin");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -233,6 +239,7 @@ __device__ Threshold radix_select_tau(Block<T>& blk, const uint32_t (&k)[R], Val
     prefix = (prefix & ~dmask) | (digit << lo);
     diff &= ~dmask;
     __syncthreads();  // bc and hist are rewritten by the next pass
+    on_pass(prefix);
     if (stop && reach <= stop) break;
   }
   return Threshold{prefix, K - above};
@@ -777,6 +784,12 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
   };
   uint32_t bound = 0;
   bool have = false;
+  // After the bound's first radix pass every candidate group has its
+  // maximum at or above the value decided so far: one score of each such
+  // group is loaded then, so that the expansion's loads find its lines in
+  // cache.  The values are not used (an empty asm statement keeps the loads).
+  float pfv[RG] = {};
+  bool pf_done = false;
   if (gm.seed) {  // a hint: valid if at least K maxima reach it, useful if at most 2 K do
     const uint32_t hint = gm.tau[row];
     if (hint != 0u) {
@@ -797,8 +810,17 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
       kk[i] = k1[i];
       kk[RG + i] = k2[i];
     }
+    auto touch = [&](uint32_t pre) {  // after the first pass only
+      if (pf_done) return;
+      pf_done = true;
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        const int j = i * T + (int)threadIdx.x;
+        pfv[i] = i < n_slots && j < G && k1[i] != 0u && k1[i] >= pre ? src[16 * j] : 0.f;
+      }
+    };
     bound = radix_select_tau(blk, kk, [&](int i) { return (i % RG) < n_slots; }, (uint32_t)K,
-                             (uint32_t)K + (uint32_t)K / 4, cg, sc).tau;
+                             (uint32_t)K + (uint32_t)K / 4, cg, sc, touch).tau;
   }
 
   // ---- 2a. candidate groups (maximum >= bound), in position order
@@ -861,6 +883,8 @@ __global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(
       }
       cnt[r] = (uint32_t)__popc(hit[r]);
     }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) asm volatile("" ::"v"(pfv[i]));  // the early loads (done by now)
     m = slot_major_offsets(cnt, rounds, eoff, sc);
     if (m <= (uint32_t)kFusedList) {
       // the hits of each group, lowest position first; a hit's score is
