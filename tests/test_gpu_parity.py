@@ -614,6 +614,19 @@ def test_fused_topk_ties_in_the_candidate_list(K, n_a, n_b):
         kept, np.concatenate([13 * np.arange(n_a), 30000 + 13 * np.arange(K - n_a)]))
 
 
+def test_fused_topk_negative_and_zero_scores():
+    """Scores at or below zero, where the expansion forms keys instead of
+    comparing raw bits: one row with every head weight negated (scores
+    -w . relu(q . k): zeros of both signs and negative values), one with
+    weights of alternating sign (both signs), one as generated."""
+    lens = [20000, 70000, 131072]
+    wl = dsa_synth.latent("fused_negative", "decode", lens, seed=76, topk=2048, H_idx=64)
+    hc = dsa_synth.host_case(wl, with_kv=False)
+    hc.w[0] = -hc.w[0]
+    hc.w[1, 1::2] = -hc.w[1, 1::2]
+    _fused_case(wl, hc, "scores <= 0 and of both signs")
+
+
 def test_fused_topk_small_K():
     # K = 37: rows have at least 4 K groups, the bound comes from the group
     # maxima alone; the longest row uses every group slot of the kernel
