@@ -76,6 +76,18 @@ def test_small_family_many_splits():
     check_decode(wl)
 
 
+def test_latent_decode_empty_and_tiny_sequences():
+    # one latent decode batch through the fused chain: a sequence with no
+    # cached position (nothing to select: idx all -1, out 0, lse -inf), one
+    # and two positions, a 16-position group and one past it, rows around K
+    wl = dsa_synth.latent("latent_tiny", "decode", [0, 1, 2, 16, 17, 2047, 2048, 2049], seed=91,
+                          topk=2048)
+    _, step = check_decode(wl)
+    assert torch.all(step.idx[0] == -1)
+    assert torch.all(step.out[0] == 0) and torch.all(torch.isneginf(step.lse[0]))
+    assert torch.all(step.idx[1, 1:] == -1) and step.idx[1, 0].item() == 0
+
+
 def test_latent_decode_short_rows():
     # rows <= 16384 take the one-workgroup-per-row Top-K path
     wl = dsa_synth.latent("latent_short", "decode", [700, 2048, 2049, 5000, 9001], seed=22,
